@@ -1,0 +1,903 @@
+// HIP kernels of libjsverify for gfx950 (MI355X).
+//
+//   stats_kernel   fused final RMSNorm + LM head (bf16 MFMA 16x16x32, or f32 MFMA 16x16x4)
+//                  with an epilogue that writes the logits and per-row online softmax
+//                  statistics; the last workgroup to finish combines the statistics and
+//                  runs the acceptance scan (JetSpec++ paper §3, App. F.3) or the outcome
+//                  marginals (§4.2 Eq. 6).
+//   sample_kernel  bonus token of each request by inverse CDF over the residual of the
+//                  rejected row (§3), spread over vocabulary slices; the last slice to
+//                  finish locates the CDF step.
+//   score_kernel   per (request, row, slice) residual mass and top-(N+1) candidates; the
+//                  last workgroup of a request merges them into the top-N outcomes (§4.2
+//                  Eq. 7, App. B.1).
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+
+#include "jsv_internal.h"
+#include "jsverify.h"
+
+namespace jsv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr double kAcceptTie = 1e-4;
+constexpr float kLogitGapTie = 1e-3f;
+constexpr double kCdfTie = 1e-8;
+constexpr double kTopNTie = 1e-3;
+
+// ------------------------------------------------------------------------------------
+// Philox4x32-10, from the SC'11 paper by Salmon, Moraes, Dror and Shaw.
+// Counter (row i, request b, lo32(offset), hi32(offset)), key (lo32(seed), hi32(seed)).
+__device__ inline void philox4x32_10(uint32_t ctr[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * ctr[0], hi0 = __umulhi(0xD2511F53u, ctr[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * ctr[2], hi1 = __umulhi(0xCD9E8D57u, ctr[2]);
+    const uint32_t n0 = hi1 ^ ctr[1] ^ k0;
+    const uint32_t n2 = hi0 ^ ctr[3] ^ k1;
+    ctr[0] = n0; ctr[1] = lo1; ctr[2] = n2; ctr[3] = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// u: acceptance uniform (x0 / 2^32); v: bonus uniform with 53 random bits.
+__device__ inline void row_uniforms(uint64_t seed, uint64_t offset, int b, int i, double& u,
+                                    double& v) {
+  uint32_t c[4] = {uint32_t(i), uint32_t(b), uint32_t(offset), uint32_t(offset >> 32)};
+  philox4x32_10(c, uint32_t(seed), uint32_t(seed >> 32));
+  u = double(c[0]) * 0x1p-32;
+  v = double((uint64_t(c[1]) << 21) | uint64_t(c[2] >> 11)) * 0x1p-53;
+}
+
+// ------------------------------------------------------------------------------------
+// Element helpers.
+__device__ inline float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+__device__ inline uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<JSV_BF16> { static constexpr int EPL = 8, ESZ = 2; };
+template <> struct Elem<JSV_F32> { static constexpr int EPL = 4, ESZ = 4; };
+
+template <int DT>
+__device__ inline void unpack(const uint4& q, float* x) {
+  if constexpr (DT == JSV_BF16) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_to_f32(w[e] & 0xffffu);
+      x[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+    }
+  } else {
+    x[0] = __uint_as_float(q.x); x[1] = __uint_as_float(q.y);
+    x[2] = __uint_as_float(q.z); x[3] = __uint_as_float(q.w);
+  }
+}
+
+// x = round_dtype( fp32( fp32(h * r) * gamma ) ) for one 16-byte group of elements.
+template <int DT>
+__device__ inline uint4 norm_pack(const uint4& hq, const uint4& gq, float r) {
+  constexpr int EPL = Elem<DT>::EPL;
+  float h[EPL], g[EPL];
+  unpack<DT>(hq, h);
+  unpack<DT>(gq, g);
+  float y[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const float t = __fmul_rn(h[e], r);
+    y[e] = __fmul_rn(t, g[e]);
+  }
+  if constexpr (DT == JSV_BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = f32_to_bf16_rne(y[2 * e]) | (f32_to_bf16_rne(y[2 * e + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    return make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                      __float_as_uint(y[3]));
+  }
+}
+
+// acc += A(16x(k-step)) * B((k-step)x16).  Lane l holds row l%16 of A and column l%16 of
+// B over the same k positions (lane group l/16 owns k = 8*(l/16)..+7 for bf16, 4 elements
+// consumed by four 16x16x4 steps for f32), so any hardware k order gives the same sum.
+template <int DT>
+__device__ inline floatx4 mfma_step(const uint4& a, const uint4& b, floatx4 acc) {
+  if constexpr (DT == JSV_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    return acc;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Online softmax statistics.  (m, s) means s = sum exp((z - m)/T); top2 is the second
+// largest value; idx the argmax with the lowest id among equal maxima.
+struct Stat {
+  float m, top2, mq;
+  int idx;
+  double s, sq;
+  uint32_t flags;
+};
+
+__device__ inline void stat_init(Stat& st) {
+  st.m = -INFINITY; st.top2 = -INFINITY; st.mq = -INFINITY;
+  st.idx = INT_MAX; st.s = 0.0; st.sq = 0.0; st.flags = 0;
+}
+
+__device__ inline void ms_merge(float& m, double& s, float mo, double so, float c) {
+  const float nm = fmaxf(m, mo);
+  if (nm == -INFINITY) { m = nm; s = 0.0; return; }
+  s = s * double(exp2f((m - nm) * c)) + so * double(exp2f((mo - nm) * c));
+  m = nm;
+}
+
+__device__ inline void stat_merge(Stat& a, const Stat& b, float c, bool soft) {
+  const bool take = (b.m > a.m) || (b.m == a.m && b.idx < a.idx);
+  const float top2 = take ? fmaxf(b.top2, a.m) : fmaxf(a.top2, b.m);
+  if (soft) {
+    ms_merge(a.m, a.s, b.m, b.s, c);
+    ms_merge(a.mq, a.sq, b.mq, b.sq, c);
+  }
+  if (take) { a.m = b.m; a.idx = b.idx; }
+  a.top2 = top2;
+  a.flags |= b.flags;
+}
+
+__device__ inline Stat stat_shfl_xor(const Stat& a, int mask) {
+  Stat o;
+  o.m = __shfl_xor(a.m, mask);
+  o.top2 = __shfl_xor(a.top2, mask);
+  o.mq = __shfl_xor(a.mq, mask);
+  o.idx = __shfl_xor(a.idx, mask);
+  o.s = __shfl_xor(a.s, mask);
+  o.sq = __shfl_xor(a.sq, mask);
+  o.flags = __shfl_xor(a.flags, mask);
+  return o;
+}
+
+__device__ inline Stat stat_load(const RowStat& r) {
+  Stat s;
+  s.m = r.m; s.top2 = r.top2; s.mq = r.mq; s.idx = r.idx; s.s = r.s; s.sq = r.sq; s.flags = r.flags;
+  return s;
+}
+
+// ------------------------------------------------------------------------------------
+// Last-workgroup finalize of the LM-head kernel: combine every workgroup's partial
+// statistics, then per request run the acceptance scan (verify) or the outcome
+// marginals (score).  Runs in one workgroup of kThreads threads.
+__device__ void finalize_block(const StatsArgs& a, int P, Stat* rows_sh) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const bool soft = a.T > 0.f;
+  const float c = a.c;
+  const int M = a.M;
+  // Phase A: row r is combined by wave r % kWaves; lanes stride over the partials.
+  for (int r0 = w; r0 < M; r0 += 2 * kWaves) {
+    Stat acc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) stat_init(acc[u]);
+#pragma unroll 4
+    for (int p = lane; p < P; p += kWave) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = r0 + u * kWaves;
+        if (r < M) stat_merge(acc[u], stat_load(a.partial[(size_t)p * M + r]), c, soft);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      for (int off = 32; off > 0; off >>= 1) stat_merge(acc[u], stat_shfl_xor(acc[u], off), c, soft);
+      const int r = r0 + u * kWaves;
+      if (lane == 0 && r < M) rows_sh[r] = acc[u];
+    }
+  }
+  __syncthreads();
+  if (a.K < 0) return;
+
+  // Phase B: wave b handles request b; lane i handles row i.
+  const int K = a.K, R = K + 1;
+  const int64_t V = a.V;
+  for (int b = w; b < a.B; b += kWaves) {
+    const bool act = lane <= K;
+    const int row = b * R + lane;
+    Stat st;
+    stat_init(st);
+    if (act) st = rows_sh[row];
+    const int di = (lane < K) ? a.drafts[b * K + lane] : -1;
+    const bool bad = act && ((st.flags & JSV_FLAG_INVALID) || (lane < K && (di < 0 || (int64_t)di >= V)));
+    const bool invalid = __ballot(bad) != 0;
+    if (invalid) {
+      if (act && a.finalize == kFinalizeVerify) a.committed[row] = -1;
+      if (lane == 0) {
+        if (a.finalize == kFinalizeVerify) a.n_accepted[b] = -1;
+        if (a.flags) a.flags[b] = JSV_FLAG_INVALID;
+        ReqState rq{}; rq.k = -1; rq.flags = JSV_FLAG_INVALID; a.req[b] = rq;
+      }
+      if (a.finalize == kFinalizeScore) {
+        if (lane < a.top_n) {
+          a.out_len[b * a.top_n + lane] = -1;
+          a.out_token[b * a.top_n + lane] = -1;
+          a.out_prob[b * a.top_n + lane] = 0.f;
+        }
+        if (act && a.len_marginal) a.len_marginal[row] = 0.0;
+      }
+      continue;
+    }
+
+    double alpha = 0.0;
+    if (!soft) {
+      // Greedy verification: accept while the draft equals the row's argmax.
+      alpha = (lane < K && di == st.idx) ? 1.0 : 0.0;
+    } else if (lane < K) {
+      const float zd = a.zd[row];
+      const double pd = double(exp2f((zd - st.m) * c)) / st.s;
+      if (a.mode == JSV_PROPOSAL_POINT) {
+        alpha = pd;
+      } else {
+        const float gd = a.G[(size_t)(b * K + lane) * V + di];
+        const double qd = double(exp2f((gd - st.mq) * c)) / st.sq;
+        alpha = (pd == 0.0) ? 0.0 : (pd >= qd ? 1.0 : pd / qd);
+      }
+    }
+
+    uint32_t f = 0;
+    int k = K;
+    double vk = 0.0;
+    if (!soft) {
+      const uint64_t rej = __ballot(lane < K && alpha == 0.0);
+      k = rej ? __builtin_ctzll(rej) : K;
+      const bool gap = act && lane <= k && (st.m - st.top2) < kLogitGapTie;
+      if (__ballot(gap)) f |= JSV_FLAG_LOGIT_GAP;
+    } else if (a.finalize == kFinalizeVerify) {
+      double u = 0.0, v = 0.0;
+      if (act) row_uniforms(a.seed, a.offset, b, lane, u, v);
+      const uint64_t rej = __ballot(lane < K && !(u < alpha));
+      k = rej ? __builtin_ctzll(rej) : K;
+      const bool tie = lane < K && lane <= k && fabs(u - alpha) < kAcceptTie;
+      if (__ballot(tie)) f |= JSV_FLAG_ACCEPT_TIE;
+      vk = __shfl(v, k);
+    }
+    const int bonus = __shfl(st.idx, k);
+
+    // A_i = prod_{j<i} alpha_j (probability of reaching row i).
+    double A = 1.0;
+    for (int j = 0; j < K; ++j) {
+      const double aj = __shfl(alpha, j);
+      if (j < lane) A *= aj;
+    }
+
+    if (act) {
+      RowFinal rf{};
+      rf.s = st.s; rf.sq = st.sq; rf.alpha = alpha; rf.A = A;
+      rf.m = st.m; rf.top2 = st.top2; rf.mq = st.mq; rf.idx = st.idx; rf.flags = st.flags;
+      a.rowfinal[row] = rf;
+    }
+    if (a.finalize == kFinalizeVerify) {
+      if (act) a.committed[row] = (lane < k) ? di : ((lane == k && !soft) ? bonus : -1);
+      if (lane == 0) {
+        a.n_accepted[b] = k;
+        if (a.flags) a.flags[b] = f;
+        ReqState rq{}; rq.vk = vk; rq.k = k; rq.flags = f; a.req[b] = rq;
+      }
+    } else {  // score
+      if (act && a.len_marginal) {
+        a.len_marginal[row] = soft ? ((lane < K) ? A * (1.0 - alpha) : A) : (lane == k ? 1.0 : 0.0);
+      }
+      if (!soft) {  // all mass on the greedy outcome
+        if (lane < a.top_n) {
+          a.out_len[b * a.top_n + lane] = (lane == 0) ? k : -1;
+          a.out_token[b * a.top_n + lane] = (lane == 0) ? bonus : -1;
+          a.out_prob[b * a.top_n + lane] = (lane == 0) ? 1.f : 0.f;
+        }
+      }
+      if (lane == 0) {
+        if (a.flags) a.flags[b] = f;
+        ReqState rq{}; rq.k = k; rq.flags = f; a.req[b] = rq;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Fused RMSNorm + LM head + statistics.  Workgroup wg owns 16-row vocabulary groups
+// [g0, g1); its 8 waves split d into equal k-slices, each wave keeping the normalised
+// hidden states of its slice in registers and streaming the same slice of W straight
+// into MFMA operands, D k-steps ahead.  Per group the 8 partial 16 x (16*NT) tiles are
+// summed through LDS (in fp64, fixed order) and thread (token jj, column ii) folds its
+// logit into running statistics.
+template <int DT, int NT, int NKS, int D>
+__global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
+  constexpr int EPL = Elem<DT>::EPL, ESZ = Elem<DT>::ESZ, KS = 4 * EPL;
+  static_assert(D >= 1 && D <= NKS, "prefetch window");
+  __shared__ floatx4 red[2][kWaves][NT][kWave];
+  __shared__ float rnorm[kRowsPerPass];
+  __shared__ uint32_t last_flag;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int P = gridDim.x, wg = blockIdx.x;
+  const int64_t V = a.V;
+  const int d = a.d;
+  const int64_t ngroups = (V + 15) >> 4;
+  const int64_t g0 = ngroups * wg / P, g1 = ngroups * (wg + 1) / P;
+  const int kb = w * (NKS * KS) + (lane >> 4) * EPL;
+  const char* Wb = static_cast<const char*>(a.W);
+  const int vr = lane & 15;
+
+  auto wload = [&](int64_t g, int s) -> uint4 {
+    const int64_t v = g * 16 + vr;
+    uint4 q = make_uint4(0u, 0u, 0u, 0u);
+    if (v < V) q = *reinterpret_cast<const uint4*>(Wb + ((size_t)v * d + kb + s * KS) * ESZ);
+    return q;
+  };
+
+  // Start streaming W before the norm prologue.
+  uint4 fr[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) fr[j] = (g0 < g1) ? wload(g0, j) : make_uint4(0u, 0u, 0u, 0u);
+
+  // RMSNorm factors r = 1 / sqrt(mean(h^2) + eps) of the rows of this pass.
+  const char* Hb = static_cast<const char*>(a.hidden);
+  for (int r = w; r < a.rows; r += kWaves) {
+    const char* hr = Hb + (size_t)(a.row0 + r) * d * ESZ;
+    float ss = 0.f;
+    for (int k = lane * EPL; k < d; k += kWave * EPL) {
+      float x[EPL];
+      unpack<DT>(*reinterpret_cast<const uint4*>(hr + (size_t)k * ESZ), x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ss = fmaf(x[e], x[e], ss);
+    }
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) rnorm[r] = 1.0f / sqrtf(ss / float(d) + a.eps);
+  }
+  __syncthreads();
+
+  // Normalised hidden states of this wave's k-slice, in MFMA B-operand layout.
+  uint4 xf[NT][NKS];
+  const char* Gm = static_cast<const char*>(a.gamma);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tok = t * 16 + (lane & 15);
+    const bool ok = tok < a.rows;
+    const float r = ok ? rnorm[tok] : 0.f;
+    const char* hr = Hb + (size_t)(a.row0 + (ok ? tok : 0)) * d * ESZ;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const int k = kb + s * KS;
+      if (ok) {
+        const uint4 hq = *reinterpret_cast<const uint4*>(hr + (size_t)k * ESZ);
+        const uint4 gq = *reinterpret_cast<const uint4*>(Gm + (size_t)k * ESZ);
+        xf[t][s] = norm_pack<DT>(hq, gq, r);
+      } else {
+        xf[t][s] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+
+  // Epilogue identity: token jj of this pass, vocabulary column ii of the group.
+  const int jj = tid >> 4, ii = tid & 15;
+  const bool tok_ok = jj < a.rows;
+  const int row = a.row0 + (tok_ok ? jj : 0);
+  bool draft = false;
+  int dtok = -1;
+  const float* grow = nullptr;
+  if (a.K >= 0 && tok_ok) {
+    const int b = row / (a.K + 1), i = row - b * (a.K + 1);
+    draft = i < a.K;
+    if (draft) {
+      dtok = a.drafts[b * a.K + i];
+      if (a.want_q) grow = a.G + (size_t)(b * a.K + i) * V;
+    }
+  }
+  const bool soft = a.T > 0.f;
+  const float c = a.c;
+  Stat st;
+  stat_init(st);
+  float* lrow = a.logits + (size_t)row * V;
+
+  int buf = 0;
+  for (int64_t g = g0; g < g1; ++g) {
+    const int64_t v = g * 16 + ii;
+    float gv = 0.f;
+    const bool gok = grow != nullptr && v < V;
+    if (gok) gv = grow[v];
+    floatx4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const uint4 f = fr[s % D];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = mfma_step<DT>(f, xf[t][s], acc[t]);
+      const bool nxt = (s + D) >= NKS;
+      const int sn = nxt ? (s + D - NKS) : (s + D);
+      const int64_t gn = g + (nxt ? 1 : 0);
+      if (gn < g1) fr[s % D] = wload(gn, sn);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[buf][w][t][lane] = acc[t];
+    __syncthreads();
+    if (jj < NT * 16) {
+      const int t = jj >> 4, src = ((ii >> 2) << 4) + (jj & 15), r = ii & 3;
+      double zz = 0.0;
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2) zz += double(red[buf][w2][t][src][r]);
+      const float z = float(zz);
+      if (tok_ok && v < V) {
+        lrow[v] = z;
+        if (a.stats) {
+          if (!(fabsf(z) <= FLT_MAX)) {
+            st.flags |= JSV_FLAG_INVALID;
+          } else if (z > st.m) {
+            if (soft) st.s = st.s * double(exp2f((st.m - z) * c)) + 1.0;
+            st.top2 = st.m; st.m = z; st.idx = int(v);
+          } else {
+            st.top2 = fmaxf(st.top2, z);
+            if (soft) st.s += double(exp2f((z - st.m) * c));
+          }
+          if (draft && v == dtok) a.zd[row] = z;
+          if (gok) {
+            if (!(fabsf(gv) <= FLT_MAX)) {
+              st.flags |= JSV_FLAG_INVALID;
+            } else if (gv > st.mq) {
+              st.sq = st.sq * double(exp2f((st.mq - gv) * c)) + 1.0;
+              st.mq = gv;
+            } else {
+              st.sq += double(exp2f((gv - st.mq) * c));
+            }
+          }
+        }
+      }
+    }
+    buf ^= 1;
+  }
+
+  if (!a.stats) return;
+  for (int off = 1; off < 16; off <<= 1) stat_merge(st, stat_shfl_xor(st, off), c, soft);
+  if (ii == 0 && tok_ok) {
+    RowStat rs{};
+    rs.s = st.s; rs.sq = st.sq; rs.m = st.m; rs.top2 = st.top2; rs.mq = st.mq;
+    rs.idx = st.idx; rs.flags = st.flags;
+    a.partial[(size_t)wg * a.M + row] = rs;
+  }
+  if (a.finalize == kFinalizeNone) return;
+
+  // Last workgroup to arrive finalizes (no waiting: the others simply exit).
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last_flag = (atomicAdd(a.counter, 1u) == uint32_t(P - 1)) ? 1u : 0u;
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  __shared__ Stat rows_sh[kMaxB * (kMaxK + 1)];
+  finalize_block(a, P, rows_sh);
+  if (tid == 0) *a.counter = 0u;
+}
+
+// ------------------------------------------------------------------------------------
+// Block-level helpers for the slice kernels (kSliceThreads = 256 = 4 waves).
+__device__ inline double block_sum(double x, double* sh) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) sh[w] = x;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < kSliceThreads / kWave; ++i) t += sh[i];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix sum over the block in thread order (deterministic).
+__device__ inline double block_exclusive_scan(double x, double* sh) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double inc = x;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) sh[w] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int i = 0; i < w; ++i) base += sh[i];
+  __syncthreads();
+  return base + inc - x;
+}
+
+__device__ inline int block_min_int(int x, int* sh) {
+  for (int off = 32; off > 0; off >>= 1) x = min(x, __shfl_xor(x, off));
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) sh[w] = x;
+  __syncthreads();
+  int t = INT_MAX;
+  for (int i = 0; i < kSliceThreads / kWave; ++i) t = min(t, sh[i]);
+  __syncthreads();
+  return t;
+}
+
+__device__ inline int block_max_int(int x, int* sh) { return -block_min_int(-x, sh); }
+
+// Residual value r(v) and target probability p(v) of row k (paper §3; App. F.3).
+struct RowModel {
+  float m, mq, c;
+  double s, sq;
+  bool use_q;
+  int dk;
+  __device__ inline void eval(int64_t v, float z, float g, double& r, double& p) const {
+    p = double(exp2f((z - m) * c)) / s;
+    if (use_q) {
+      const double q = double(exp2f((g - mq) * c)) / sq;
+      r = p > q ? p - q : 0.0;
+    } else {
+      r = (v == dk) ? 0.0 : p;
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------
+// Bonus sampler: grid (slices, B).  Each slice sums the residual of row k over its
+// columns; the last slice of a request locates t = v_k * Z in the slice totals, then
+// re-walks that slice with a block prefix sum to the first column whose CDF exceeds t.
+__global__ __launch_bounds__(kSliceThreads) void sample_kernel(SampleArgs a) {
+  const int b = blockIdx.y, j = blockIdx.x, NB = gridDim.x, tid = threadIdx.x;
+  const ReqState rq = a.req[b];
+  if (!(a.T > 0.f) || rq.k < 0) return;
+  const int K = a.K, k = rq.k, row = b * (K + 1) + k;
+  const RowFinal rf = a.rowfinal[row];
+  const int64_t V = a.V;
+  const float* zr = a.logits + (size_t)row * V;
+  RowModel rm;
+  rm.m = rf.m; rm.mq = rf.mq; rm.c = a.c; rm.s = rf.s; rm.sq = rf.sq;
+  rm.use_q = (a.mode == JSV_PROPOSAL_SOFTMAX) && k < K;
+  rm.dk = (a.mode == JSV_PROPOSAL_POINT && k < K) ? a.drafts[b * K + k] : -1;
+  const float* gr = rm.use_q ? a.G + (size_t)(b * K + k) * V : nullptr;
+  const int64_t L = (V + NB - 1) / NB;
+
+  __shared__ float zsh[kSampleMaxSlice];
+  __shared__ float gsh[kSampleMaxSlice];
+  __shared__ double dsh[8];
+  __shared__ int ish[8];
+  __shared__ uint32_t last_flag;
+  __shared__ double bc_t, bc_base, bc_Z, bc_clo, bc_chi;
+  __shared__ int bc_s, bc_zero, bc_fall;
+
+  auto stage = [&](int64_t v0, int n) {
+    for (int e = tid; e < n; e += kSliceThreads) {
+      zsh[e] = zr[v0 + e];
+      if (gr) gsh[e] = gr[v0 + e];
+    }
+    __syncthreads();
+  };
+
+  {
+    const int64_t v0 = (int64_t)j * L;
+    const int n = (int)max<int64_t>(0, min<int64_t>(V, v0 + L) - v0);
+    stage(v0, n);
+    const int E = (n + kSliceThreads - 1) / kSliceThreads;
+    const int e0 = tid * E, e1 = min(n, e0 + E);
+    double rs = 0.0, ps = 0.0;
+    for (int e = e0; e < e1; ++e) {
+      double r, p;
+      rm.eval(v0 + e, zsh[e], gr ? gsh[e] : 0.f, r, p);
+      rs += r;
+      ps += p;
+    }
+    rs = block_sum(rs, dsh);
+    ps = block_sum(ps, dsh);
+    if (tid == 0) {
+      a.zs[((size_t)b * NB + j) * 2 + 0] = rs;
+      a.zs[((size_t)b * NB + j) * 2 + 1] = ps;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last_flag = (atomicAdd(&a.counter[b], 1u) == uint32_t(NB - 1)) ? 1u : 0u;
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+
+  uint32_t f = 0;
+  if (tid == 0) {
+    const double* zs = a.zs + (size_t)b * NB * 2;
+    double Zr = 0.0, Zp = 0.0;
+    for (int q = 0; q < NB; ++q) { Zr += zs[2 * q]; Zp += zs[2 * q + 1]; }
+    const int zero = (Zr > 0.0) ? 0 : 1;
+    const double Z = zero ? Zp : Zr;
+    const double t = rq.vk * Z;
+    double cum = 0.0, base = 0.0;
+    int s = -1, last_nz = 0;
+    for (int q = 0; q < NB; ++q) {
+      const double x = zs[2 * q + zero];
+      if (x > 0.0) last_nz = q;
+      if (s < 0 && x > 0.0 && cum + x > t) { s = q; base = cum; }
+      cum += x;
+    }
+    int fall = 0;
+    if (s < 0) {  // rounding left t at or above the last CDF value
+      s = last_nz;
+      fall = 1;
+      double c2 = 0.0;
+      for (int q = 0; q < s; ++q) c2 += zs[2 * q + zero];
+      base = c2;
+    }
+    bc_t = t; bc_base = base; bc_Z = Z; bc_s = s; bc_zero = zero; bc_fall = fall;
+  }
+  __syncthreads();
+  const int s = bc_s, zero = bc_zero;
+  const double t = bc_t, Z = bc_Z;
+  if (zero) f |= JSV_FLAG_ZERO_RESIDUAL;
+  const int64_t v0 = (int64_t)s * L;
+  const int n = (int)max<int64_t>(0, min<int64_t>(V, v0 + L) - v0);
+  stage(v0, n);
+  const int E = (n + kSliceThreads - 1) / kSliceThreads;
+  const int e0 = tid * E, e1 = min(n, e0 + E);
+  double mine = 0.0;
+  for (int e = e0; e < e1; ++e) {
+    double r, p;
+    rm.eval(v0 + e, zsh[e], gr ? gsh[e] : 0.f, r, p);
+    mine += zero ? p : r;
+  }
+  double C = bc_base + block_exclusive_scan(mine, dsh);
+  int found = INT_MAX, last_pos = -1;
+  double clo = 0.0, chi = 0.0;
+  for (int e = e0; e < e1; ++e) {
+    double r, p;
+    rm.eval(v0 + e, zsh[e], gr ? gsh[e] : 0.f, r, p);
+    const double x = zero ? p : r;
+    const double Cn = C + x;
+    if (x > 0.0) last_pos = int(v0 + e);
+    if (found == INT_MAX && x > 0.0 && Cn > t) { found = int(v0 + e); clo = C; chi = Cn; }
+    C = Cn;
+  }
+  int tok = block_min_int(found, ish);
+  if (tok != INT_MAX && found == tok) { bc_clo = clo; bc_chi = chi; }
+  const int lastp = block_max_int(last_pos, ish);
+  __syncthreads();
+  if (tid == 0) {
+    if (tok == INT_MAX || bc_fall) {
+      tok = lastp;
+      f |= JSV_FLAG_CDF_TIE;
+    } else if ((t - bc_clo) < kCdfTie * Z || (bc_chi - t) < kCdfTie * Z) {
+      f |= JSV_FLAG_CDF_TIE;
+    }
+    a.committed[row] = tok;
+    if (a.flags) a.flags[b] |= f;
+    a.counter[b] = 0u;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Outcome scorer: grid (slices, K+1, B).  Each (row k, slice) computes its residual mass
+// and its top-(N+1) columns by (r desc, p desc, token asc); the last workgroup of a
+// request turns candidates into P(k, a) and selects the top-N by (P desc, k asc, a asc).
+struct Key {
+  double r, p;
+  int v;
+};
+__device__ inline bool key_better(const Key& x, const Key& y) {
+  if (x.r != y.r) return x.r > y.r;
+  if (x.p != y.p) return x.p > y.p;
+  return x.v < y.v;
+}
+
+__device__ inline Key block_best(Key k, Key* sh) {
+  for (int off = 32; off > 0; off >>= 1) {
+    Key o;
+    o.r = __shfl_xor(k.r, off); o.p = __shfl_xor(k.p, off); o.v = __shfl_xor(k.v, off);
+    if (key_better(o, k)) k = o;
+  }
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) sh[w] = k;
+  __syncthreads();
+  Key best = sh[0];
+  for (int i = 1; i < kSliceThreads / kWave; ++i)
+    if (key_better(sh[i], best)) best = sh[i];
+  __syncthreads();
+  return best;
+}
+
+__global__ __launch_bounds__(kSliceThreads) void score_kernel(ScoreArgs a) {
+  const int b = blockIdx.z, k = blockIdx.y, j = blockIdx.x, NB = gridDim.x, tid = threadIdx.x;
+  const ReqState rq = a.req[b];
+  if (!(a.T > 0.f) || rq.k < 0) return;
+  const int K = a.K, R = K + 1, row = b * R + k, N1 = a.top_n + 1;
+  const RowFinal rf = a.rowfinal[row];
+  const int64_t V = a.V;
+  const double Pk = (k < K) ? rf.A * (1.0 - rf.alpha) : rf.A;
+  RowModel rm;
+  rm.m = rf.m; rm.mq = rf.mq; rm.c = a.c; rm.s = rf.s; rm.sq = rf.sq;
+  rm.use_q = (a.mode == JSV_PROPOSAL_SOFTMAX) && k < K;
+  rm.dk = (a.mode == JSV_PROPOSAL_POINT && k < K) ? a.drafts[b * K + k] : -1;
+  const float* zr = a.logits + (size_t)row * V;
+  const float* gr = rm.use_q ? a.G + (size_t)(b * K + k) * V : nullptr;
+  const int64_t L = (V + NB - 1) / NB;
+  const int64_t v0 = (int64_t)j * L;
+  const int n = (int)max<int64_t>(0, min<int64_t>(V, v0 + L) - v0);
+
+  __shared__ double rsh[kScoreMaxSlice];
+  __shared__ double psh[kScoreMaxSlice];
+  __shared__ double dsh[8];
+  __shared__ Key ksh[8];
+  __shared__ uint32_t last_flag;
+
+  Cand* cand = a.cand + ((size_t)row * NB + j) * N1;
+  if (Pk > 0.0) {
+    for (int e = tid; e < n; e += kSliceThreads) {
+      double r, p;
+      rm.eval(v0 + e, zr[v0 + e], gr ? gr[v0 + e] : 0.f, r, p);
+      rsh[e] = r;
+      psh[e] = p;
+    }
+    __syncthreads();
+    const int E = (n + kSliceThreads - 1) / kSliceThreads;
+    const int e0 = tid * E, e1 = min(n, e0 + E);
+    double rs = 0.0;
+    for (int e = e0; e < e1; ++e) rs += rsh[e];
+    rs = block_sum(rs, dsh);
+    if (tid == 0) a.zs[(size_t)row * NB + j] = rs;
+    Key thr{INFINITY, INFINITY, -1};
+    for (int q = 0; q < N1; ++q) {
+      Key best{-1.0, -1.0, INT_MAX};
+      for (int e = e0; e < e1; ++e) {
+        const Key x{rsh[e], psh[e], int(v0 + e)};
+        if (key_better(thr, x) && key_better(x, best)) best = x;
+      }
+      best = block_best(best, ksh);
+      if (tid == 0) {
+        Cand cd{};
+        cd.r = best.r; cd.p = best.p; cd.tok = (best.v == INT_MAX) ? -1 : best.v;
+        cand[q] = cd;
+      }
+      thr = best;
+    }
+  } else {
+    if (tid == 0) a.zs[(size_t)row * NB + j] = 0.0;
+    for (int q = tid; q < N1; q += kSliceThreads) {
+      Cand cd{};
+      cd.r = -1.0; cd.p = -1.0; cd.tok = -1;
+      cand[q] = cd;
+    }
+  }
+
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last_flag = (atomicAdd(&a.counter[b], 1u) == uint32_t(R * NB - 1)) ? 1u : 0u;
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+
+  // Merge: scale_k turns a candidate of row k into P(k, a).
+  __shared__ double scale_sh[kMaxK + 1];
+  __shared__ int usep_sh[kMaxK + 1];
+  __shared__ uint32_t flag_sh;
+  if (tid == 0) flag_sh = 0u;
+  __syncthreads();
+  for (int kk = tid; kk < R; kk += kSliceThreads) {
+    const RowFinal f2 = a.rowfinal[b * R + kk];
+    const double P2 = (kk < K) ? f2.A * (1.0 - f2.alpha) : f2.A;
+    double Zk = 0.0;
+    for (int q = 0; q < NB; ++q) Zk += a.zs[((size_t)(b * R + kk)) * NB + q];
+    double sc = 0.0;
+    int usep = 0;
+    if (P2 > 0.0) {
+      if (kk == K) { sc = P2; usep = 1; }
+      else if (Zk > 0.0) { sc = P2 / Zk; }
+      else { sc = P2; usep = 1; atomicOr(&flag_sh, JSV_FLAG_ZERO_RESIDUAL); }
+    }
+    scale_sh[kk] = sc;
+    usep_sh[kk] = usep;
+  }
+  __syncthreads();
+
+  const int total = R * NB * N1;
+  const Cand* cb = a.cand + (size_t)b * R * NB * N1;
+  // Key for the merge: r := P, p := -row, v := token (so "better" = larger P, then
+  // smaller row, then smaller token).
+  Key thr{INFINITY, INFINITY, -1};
+  double prev = -1.0;
+  for (int q = 0; q < N1; ++q) {
+    Key best{-1.0, -1.0, INT_MAX};
+    for (int e = tid; e < total; e += kSliceThreads) {
+      const Cand cd = cb[e];
+      if (cd.tok < 0) continue;
+      const int kk = e / (NB * N1);
+      const double P = scale_sh[kk] * (usep_sh[kk] ? cd.p : cd.r);
+      if (!(P > 0.0)) continue;
+      const Key x{P, -double(kk), cd.tok};
+      if (key_better(thr, x) && key_better(x, best)) best = x;
+    }
+    best = block_best(best, ksh);
+    thr = best;
+    if (tid == 0) {
+      const bool have = best.v != INT_MAX;
+      if (q < a.top_n) {
+        a.out_len[b * a.top_n + q] = have ? int(-best.p) : -1;
+        a.out_token[b * a.top_n + q] = have ? best.v : -1;
+        a.out_prob[b * a.top_n + q] = have ? float(best.r) : 0.f;
+      }
+      if (have && q > 0 && prev - best.r < kTopNTie * prev) flag_sh |= JSV_FLAG_TOPN_TIE;
+      if (have) prev = best.r;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    if (a.flags) a.flags[b] |= flag_sh;
+    a.counter[b] = 0u;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Launchers.
+template <int DT, int NT, int NKS>
+static hipError_t launch_stats_t(int grid, const StatsArgs& a, hipStream_t stream) {
+  // Prefetch window: the largest of a whole, half or quarter group whose W registers fit
+  // beside the normalised hidden states (192 of the 256 VGPRs at 2 waves per SIMD).
+  constexpr int XR = NT * NKS * 4;
+  constexpr int D = (XR + NKS * 4 <= 192) ? NKS
+                  : (XR + (NKS / 2) * 4 <= 192 && NKS >= 2) ? NKS / 2
+                  : (NKS >= 4 ? NKS / 4 : 1);
+  hipLaunchKernelGGL((stats_kernel<DT, NT, NKS, D>), dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+#define JSV_NKS_LIST(X) X(1) X(2) X(4) X(8) X(12) X(16) X(20)
+
+bool stats_supported(int dtype, int nks) {
+  if (dtype != JSV_BF16 && dtype != JSV_F32) return false;
+  switch (nks) {
+#define JSV_CASE(n) case n: return true;
+    JSV_NKS_LIST(JSV_CASE)
+#undef JSV_CASE
+    default: return false;
+  }
+}
+
+template <int DT, int NT>
+static hipError_t dispatch_nks(int nks, int grid, const StatsArgs& a, hipStream_t s) {
+  switch (nks) {
+#define JSV_CASE(n) case n: return launch_stats_t<DT, NT, n>(grid, a, s);
+    JSV_NKS_LIST(JSV_CASE)
+#undef JSV_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_stats(int dtype, int nks, int ntiles, int grid, const StatsArgs& a,
+                        hipStream_t stream) {
+  if (dtype == JSV_BF16) {
+    return ntiles == 1 ? dispatch_nks<JSV_BF16, 1>(nks, grid, a, stream)
+                       : dispatch_nks<JSV_BF16, 2>(nks, grid, a, stream);
+  }
+  return ntiles == 1 ? dispatch_nks<JSV_F32, 1>(nks, grid, a, stream)
+                     : dispatch_nks<JSV_F32, 2>(nks, grid, a, stream);
+}
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(sample_kernel, dim3(sample_slices(a.V), a.B), dim3(kSliceThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(score_kernel, dim3(score_slices(a.V), a.K + 1, a.B), dim3(kSliceThreads),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace jsv

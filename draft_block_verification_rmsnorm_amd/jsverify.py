@@ -1,0 +1,242 @@
+"""Thin Python binding of libjsverify (include/jsverify.h) over ctypes.
+
+Argument marshalling only: every step of verification and scoring runs in the HIP
+kernels of the library.  Tensors are torch tensors on the GPU; the binding passes
+their device pointers and the current HIP stream.  The functions keep the C names
+without the `jsv_` prefix.  Shape, dtype and device errors raise ValueError;
+non-OK statuses from the library raise RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libjsverify.so"
+
+JSV_OK, JSV_EINVAL, JSV_EUNSUPPORTED, JSV_EWORKSPACE, JSV_EHIP = 0, -1, -2, -3, -4
+JSV_BF16, JSV_F32 = 0, 1
+PROPOSAL_SOFTMAX, PROPOSAL_POINT = 0, 1
+
+FLAG_ACCEPT_TIE = 1 << 0
+FLAG_LOGIT_GAP = 1 << 1
+FLAG_CDF_TIE = 1 << 2
+FLAG_INVALID = 1 << 3
+FLAG_ZERO_RESIDUAL = 1 << 4
+FLAG_TOPN_TIE = 1 << 5
+
+EXPORTED = ("jsv_workspace_bytes", "jsv_lmhead_logits", "jsv_verify_block", "jsv_verify_stats",
+            "jsv_verify_sample", "jsv_score_outcomes", "jsv_status_string", "jsv_version")
+
+_DTYPES = {torch.bfloat16: JSV_BF16, torch.float32: JSV_F32}
+
+
+class _Head(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("vocab", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: Path | str | None = None) -> ctypes.CDLL:
+    """Load libjsverify.so and declare its signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"{p} is not built: run `python -m draft_block_verification_rmsnorm_amd.build` "
+                           "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(str(p))
+    vp, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t)
+    hp = ctypes.POINTER(_Head)
+    lib.jsv_workspace_bytes.argtypes = [hp, i32, i32, i32]
+    lib.jsv_workspace_bytes.restype = sz
+    lib.jsv_lmhead_logits.argtypes = [hp, vp, i64, vp, vp, sz, vp]
+    lib.jsv_lmhead_logits.restype = i32
+    verify_args = [hp, vp, vp, vp, i32, i32, f32, i32, u64, u64, vp, vp, vp, vp, vp, sz, vp]
+    lib.jsv_verify_block.argtypes = verify_args
+    lib.jsv_verify_block.restype = i32
+    lib.jsv_verify_stats.argtypes = verify_args
+    lib.jsv_verify_stats.restype = i32
+    lib.jsv_verify_sample.argtypes = [hp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]
+    lib.jsv_verify_sample.restype = i32
+    lib.jsv_score_outcomes.argtypes = [hp, vp, vp, vp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp,
+                                       vp, sz, vp]
+    lib.jsv_score_outcomes.restype = i32
+    lib.jsv_status_string.argtypes = [i32]
+    lib.jsv_status_string.restype = ctypes.c_char_p
+    lib.jsv_version.argtypes = []
+    lib.jsv_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != JSV_OK:
+        msg = load_library().jsv_status_string(status).decode()
+        raise RuntimeError(f"libjsverify: {msg} (status {status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class LMHead:
+    """The target's final RMSNorm weight and LM-head weight, on one GPU."""
+
+    def __init__(self, weight: torch.Tensor, norm_weight: torch.Tensor, eps: float = 1e-6):
+        if weight.dtype not in _DTYPES:
+            raise ValueError("weight must be bfloat16 or float32")
+        _need(weight, "weight", weight.dtype)
+        _need(norm_weight, "norm_weight", weight.dtype, (weight.shape[1],), weight.device)
+        self.weight, self.norm_weight, self.eps = weight, norm_weight, float(eps)
+        self.dtype = weight.dtype
+        self.vocab, self.hidden = int(weight.shape[0]), int(weight.shape[1])
+        self._c = _Head(weight.data_ptr(), norm_weight.data_ptr(), self.vocab, self.hidden,
+                        self.eps, _DTYPES[weight.dtype])
+
+    @property
+    def device(self):
+        return self.weight.device
+
+
+def workspace_bytes(head: LMHead, batch: int, K: int, top_n: int = 0) -> int:
+    n = load_library().jsv_workspace_bytes(ctypes.byref(head._c), batch, K, top_n)
+    if n == 0:
+        raise ValueError("unsupported head or block shape")
+    return int(n)
+
+
+def new_workspace(head: LMHead, batch: int, K: int, top_n: int = 0) -> torch.Tensor:
+    """A zero-filled device workspace big enough for (batch, K, top_n)."""
+    return torch.zeros(workspace_bytes(head, batch, K, top_n), dtype=torch.uint8, device=head.device)
+
+
+def lmhead_logits(head: LMHead, hidden: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """RMSNorm + LM head of hidden [rows, d] -> fp32 logits [rows, V]."""
+    _need(hidden, "hidden", head.dtype, device=head.device)
+    if hidden.dim() != 2 or hidden.shape[1] != head.hidden:
+        raise ValueError("hidden must be [rows, hidden]")
+    rows = hidden.shape[0]
+    if out is None:
+        out = torch.empty(rows, head.vocab, dtype=torch.float32, device=head.device)
+    _need(out, "out", torch.float32, (rows, head.vocab), head.device)
+    _check(load_library().jsv_lmhead_logits(ctypes.byref(head._c), _ptr(hidden), rows, _ptr(out),
+                                            None, 0, _stream(stream)))
+    return out
+
+
+def _block_checks(head, hidden, draft_tokens, draft_logits, mode, temperature):
+    if hidden is not None:
+        _need(hidden, "hidden", head.dtype, device=head.device)
+        if hidden.dim() != 3 or hidden.shape[2] != head.hidden:
+            raise ValueError("hidden must be [B, K+1, hidden]")
+        B, K = hidden.shape[0], hidden.shape[1] - 1
+        _need(draft_tokens, "draft_tokens", torch.int32, (B, K), head.device)
+    else:
+        _need(draft_tokens, "draft_tokens", torch.int32, device=head.device)
+        B, K = draft_tokens.shape
+    if mode == PROPOSAL_SOFTMAX and temperature > 0:
+        if draft_logits is None:
+            raise ValueError("the softmax proposal needs draft_logits")
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32, (B, K, head.vocab), head.device)
+    return B, K
+
+
+class VerifyOut:
+    def __init__(self, B, K, device):
+        self.n_accepted = torch.empty(B, dtype=torch.int32, device=device)
+        self.committed = torch.empty(B, K + 1, dtype=torch.int32, device=device)
+        self.flags = torch.empty(B, dtype=torch.int32, device=device)
+
+
+def _verify_call(fn, head, hidden, draft_tokens, draft_logits, temperature, mode, seed, offset,
+                 workspace, out, logits_out, stream):
+    B, K = _block_checks(head, hidden, draft_tokens, draft_logits, mode, temperature)
+    _need(workspace, "workspace", torch.uint8, device=head.device)
+    if logits_out is not None:
+        _need(logits_out, "logits_out", torch.float32, (B, K + 1, head.vocab), head.device)
+    if out is None:
+        out = VerifyOut(B, K, head.device)
+    _check(fn(ctypes.byref(head._c), _ptr(hidden), _ptr(draft_tokens), _ptr(draft_logits), B, K,
+              float(temperature), int(mode), int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1),
+              _ptr(out.n_accepted), _ptr(out.committed), _ptr(out.flags), _ptr(logits_out),
+              _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def verify_block(head, hidden, draft_tokens, draft_logits, temperature, mode, seed, offset,
+                 workspace, out=None, logits_out=None, stream=None) -> VerifyOut:
+    """jsv_verify_block: accept/reject the drafts of every request and draw the bonus."""
+    return _verify_call(load_library().jsv_verify_block, head, hidden, draft_tokens, draft_logits,
+                        temperature, mode, seed, offset, workspace, out, logits_out, stream)
+
+
+def verify_stats(head, hidden, draft_tokens, draft_logits, temperature, mode, seed, offset,
+                 workspace, out=None, logits_out=None, stream=None) -> VerifyOut:
+    """jsv_verify_stats: first half of verify_block (norm, LM head, statistics, scan)."""
+    return _verify_call(load_library().jsv_verify_stats, head, hidden, draft_tokens, draft_logits,
+                        temperature, mode, seed, offset, workspace, out, logits_out, stream)
+
+
+def verify_sample(head, draft_tokens, draft_logits, temperature, mode, workspace, out,
+                  logits_out=None, stream=None) -> VerifyOut:
+    """jsv_verify_sample: second half of verify_block (bonus token)."""
+    B, K = _block_checks(head, None, draft_tokens, draft_logits, mode, temperature)
+    _need(workspace, "workspace", torch.uint8, device=head.device)
+    _check(load_library().jsv_verify_sample(
+        ctypes.byref(head._c), _ptr(draft_tokens), _ptr(draft_logits), B, K, float(temperature),
+        int(mode), _ptr(out.committed), _ptr(out.flags), _ptr(logits_out), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return out
+
+
+class ScoreOut:
+    def __init__(self, B, K, top_n, device):
+        self.out_len = torch.empty(B, top_n, dtype=torch.int32, device=device)
+        self.out_token = torch.empty(B, top_n, dtype=torch.int32, device=device)
+        self.out_prob = torch.empty(B, top_n, dtype=torch.float32, device=device)
+        self.len_marginal = torch.empty(B, K + 1, dtype=torch.float64, device=device)
+        self.flags = torch.empty(B, dtype=torch.int32, device=device)
+
+
+def score_outcomes(head, hidden_pred, draft_tokens, draft_logits, temperature, mode, top_n,
+                   workspace, out=None, stream=None) -> ScoreOut:
+    """jsv_score_outcomes: outcome law of the block and its top_n outcomes."""
+    B, K = _block_checks(head, hidden_pred, draft_tokens, draft_logits, mode, temperature)
+    _need(workspace, "workspace", torch.uint8, device=head.device)
+    if out is None:
+        out = ScoreOut(B, K, top_n, head.device)
+    _check(load_library().jsv_score_outcomes(
+        ctypes.byref(head._c), _ptr(hidden_pred), _ptr(draft_tokens), _ptr(draft_logits), B, K,
+        float(temperature), int(mode), int(top_n), _ptr(out.out_len), _ptr(out.out_token),
+        _ptr(out.out_prob), _ptr(out.len_marginal), _ptr(out.flags), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return out

@@ -19,7 +19,9 @@ Readings of points the pages leave open (each is listed again in the design doc):
     definition gamma * h / sqrt(mean(h^2) + eps) is used, computed in fp32 steps
     and rounded once to the weight dtype before the LM head.
   * The proposal q is the draft logits' softmax at the same temperature as p.
-  * Temperature 0 means p is the point mass on the argmax, ties to the lowest id.
+  * Temperature 0 means p is the point mass on the argmax, ties to the lowest id, and
+    verification is argmax-prefix matching: the proposal q plays no role, so at T = 0
+    both proposals give the same result (the point-mass formulas apply).
   * A zero residual mass (only possible for a draft token that q gives no mass)
     falls back to sampling the target row itself, and is flagged.
   * An invalid request (non-finite logits, draft token outside the vocabulary)
@@ -197,6 +199,9 @@ def verify_request(z, g, drafts, T, mode, u, v):
     z = np.asarray(z, dtype=np.float64)
     K = len(drafts)
     V = z.shape[1]
+    if T == 0:
+        # greedy verification compares each draft with the row's argmax; q plays no role
+        g, mode = None, PROPOSAL_POINT
     invalid = (not np.all(np.isfinite(z))) or any(not (0 <= int(d) < V) for d in drafts)
     if g is not None:
         invalid = invalid or not np.all(np.isfinite(np.asarray(g, np.float64)))
@@ -329,7 +334,7 @@ def verify_block(head, hidden, draft_tokens, draft_logits, T, mode, seed, offset
     B, K = drafts.shape
     z = block_logits(head, hidden)
     g = _as_f64(draft_logits) if draft_logits is not None else None
-    if mode == PROPOSAL_SOFTMAX and g is None:
+    if mode == PROPOSAL_SOFTMAX and g is None and T > 0:
         raise ValueError("softmax proposal needs draft logits")
     n_acc = np.zeros(B, dtype=np.int64)
     committed = np.full((B, K + 1), -1, dtype=np.int64)
@@ -352,7 +357,7 @@ def score_outcomes(head, hidden_pred, draft_tokens, draft_logits, T, mode, N):
     B, K = drafts.shape
     z = block_logits(head, hidden_pred)
     g = _as_f64(draft_logits) if draft_logits is not None else None
-    if mode == PROPOSAL_SOFTMAX and g is None:
+    if mode == PROPOSAL_SOFTMAX and g is None and T > 0:
         raise ValueError("softmax proposal needs draft logits")
     V = z.shape[-1]
     out = {"out_len": np.full((B, N), -1, np.int64), "out_token": np.full((B, N), -1, np.int64),
@@ -360,14 +365,18 @@ def score_outcomes(head, hidden_pred, draft_tokens, draft_logits, T, mode, N):
            "flags": np.zeros(B, np.int64), "tables": np.zeros((B, K + 1, V))}
     for b in range(B):
         invalid = (not np.all(np.isfinite(z[b]))) or any(not (0 <= int(d) < V) for d in drafts[b])
-        if g is not None:
+        if g is not None and mode == PROPOSAL_SOFTMAX and T > 0:
             invalid = invalid or not np.all(np.isfinite(g[b]))
         if invalid:
             out["flags"][b] = FLAG_INVALID
             continue
         P = [probs(z[b, i], T) for i in range(K + 1)]
-        Q = [probs(g[b, i], T) for i in range(K)] if mode == PROPOSAL_SOFTMAX else None
-        table, marg, f1 = outcome_table(P, Q, drafts[b], mode)
+        use_q = mode == PROPOSAL_SOFTMAX and T > 0
+        Q = [probs(g[b, i], T) for i in range(K)] if use_q else None
+        table, marg, f1 = outcome_table(P, Q, drafts[b], mode if use_q else PROPOSAL_POINT)
+        if T == 0:
+            f1 |= FLAG_LOGIT_GAP if any(top2_gap(z[b, i]) < LOGIT_GAP_TIE
+                                        for i in range(int(np.argmax(marg)) + 1)) else 0
         lens, toks, pr, f2 = top_n(table, N)
         out["out_len"][b], out["out_token"][b], out["out_prob"][b] = lens, toks, pr
         out["len_marginal"][b] = marg

@@ -28,10 +28,10 @@ _TORCH_DTYPE = {BF16: torch.bfloat16, F32: torch.float32}
 # sigma of the draft perturbation, bisected at T = 0 so that the mean number of
 # committed tokens per block (accepted drafts + 1 bonus) is about 8 at K = 16 and
 # about 14 at K = 32 (tests/tune_sigma.py prints these values).
-SIGMA_K16_D4096 = 0.107
-SIGMA_K32_D4096 = 0.060
-SIGMA_K16_D5120 = 0.107
-SIGMA_K32_D5120 = 0.060
+SIGMA_K16_D4096 = 0.0432
+SIGMA_K32_D4096 = 0.0248
+SIGMA_K16_D5120 = 0.0494
+SIGMA_K32_D5120 = 0.0311
 SIGMA_TINY = 0.5
 
 
@@ -54,7 +54,7 @@ CONFIGS = {
     "qwen8b_k16": Config("Qwen3-8B LM head d=4096 V=151936 K=16 B=1 bf16", 151936, 4096, 16, 1, BF16,
                          0.02, SIGMA_K16_D4096, 1002),
     "qwen8b_k32_b4": Config("Qwen3-8B LM head d=4096 V=151936 K=32 B=4 bf16", 151936, 4096, 32, 4, BF16,
-                            0.02, SIGMA_K32_D4096, 1004),
+                            0.02, SIGMA_K32_D4096, 1002),
     "d5120_k16_b1": Config("d=5120 V=151936 K=16 B=1 bf16", 151936, 5120, 16, 1, BF16, 0.02,
                            SIGMA_K16_D5120, 1005),
     "d5120_k32_b2": Config("d=5120 V=151936 K=32 B=2 bf16", 151936, 5120, 32, 2, BF16, 0.02,

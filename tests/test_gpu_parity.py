@@ -1,0 +1,241 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Sizes: the tiny f32 case (d=256, V=1024, K=4) over 1000 blocks; the Qwen3-8B LM-head
+shape (d=4096, V=151936, K=16, B=1) at T = 0 and 1 in both proposal modes; K=32 B=4;
+d=5120; scoring with top-8; and the edge cases (ragged vocabularies, many row passes,
+invalid inputs, top_n = 64, run-to-run bit identity).  Everything calls the C ABI through
+the ctypes binding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_block_verification_rmsnorm_amd as jsv
+import oracle
+import synth
+from parity import (Case, compare_logits, compare_score, compare_verify, new_stats, run_score,
+                    run_verify, say)
+
+pytestmark = pytest.mark.gpu
+SOFT, POINT = jsv.PROPOSAL_SOFTMAX, jsv.PROPOSAL_POINT
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    jsv.load_library()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def tiny(dev):
+    return Case(synth.head_for(synth.CONFIGS["tiny"]), dev)
+
+
+@pytest.fixture(scope="module")
+def qwen(dev):
+    return Case(synth.head_for(synth.CONFIGS["qwen8b_k16"]), dev, f64_weight=True)
+
+
+# ---- LM head ---------------------------------------------------------------------------
+@pytest.mark.parametrize("V,d,dtype,rows", [
+    (1024, 256, synth.F32, 5), (1000, 256, synth.BF16, 3), (4099, 512, synth.BF16, 17),
+    (2048, 4096, synth.BF16, 40), (777, 5120, synth.BF16, 33), (300, 1024, synth.F32, 1),
+])
+def test_lmhead_logits(dev, V, d, dtype, rows):
+    say(f"lmhead V={V} d={d} {dtype} rows={rows}")
+    head = synth.random_head(V, d, dtype, seed=V + d)
+    case = Case(head, dev)
+    g = torch.Generator().manual_seed(rows)
+    h = torch.randn(rows, d, generator=g).to(head.weight.dtype)
+    z = jsv.lmhead_logits(case.gpu, h.to(dev))
+    torch.cuda.synchronize()
+    ref = oracle.lmhead_logits(case.oh, h)
+    err = float(np.max(np.abs(z.cpu().numpy().astype(np.float64) - ref)))
+    say(f"  max |dz| = {err:.3e}")
+    assert err <= 2e-2
+    assert err <= 1e-3   # internal alarm: the expected error is ~1e-6
+
+
+# ---- verification: tiny oracle case --------------------------------------------------------
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_verify_tiny_1000_blocks(tiny, dev, T):
+    cfg = synth.CONFIGS["tiny"]
+    ws = jsv.new_workspace(tiny.gpu, 1, cfg.K)
+    st = new_stats()
+    for blk_id in range(1000):
+        if blk_id % 250 == 0:
+            say(f"tiny verify T={T} block {blk_id}")
+        blk = synth.make_block(tiny.cpu, 1, cfg.K, cfg.sigma, T, seed=blk_id)
+        got, ref = run_verify(tiny, blk, T, SOFT, 0, blk_id, ws)
+        compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+        compare_logits(got["logits"], ref["logits"], st)
+    say(f"  {st}")
+    assert st["exact"] >= 950
+
+
+@pytest.mark.parametrize("mode", [SOFT, POINT])
+def test_verify_tiny_batched_modes(tiny, dev, mode):
+    cfg = synth.CONFIGS["tiny"]
+    ws = jsv.new_workspace(tiny.gpu, 8, cfg.K)
+    st = new_stats()
+    for seed in range(20):
+        T = [0.0, 0.5, 1.0, 2.0][seed % 4]
+        say(f"tiny batched mode={mode} seed={seed} T={T}")
+        blk = synth.make_block(tiny.cpu, 8, cfg.K, cfg.sigma, T, seed=10_000 + seed)
+        got, ref = run_verify(tiny, blk, T, mode, seed, 3 * seed, ws)
+        compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+    say(f"  {st}")
+    assert st["exact"] >= 150
+
+
+# ---- verification: Qwen3-8B LM-head shape ----------------------------------------------------
+@pytest.mark.parametrize("T,mode", [(0.0, SOFT), (1.0, SOFT), (1.0, POINT)])
+def test_verify_qwen8b_k16(qwen, dev, T, mode):
+    cfg = synth.CONFIGS["qwen8b_k16"]
+    ws = jsv.new_workspace(qwen.gpu, 1, cfg.K)
+    st = new_stats()
+    for seed in range(3):
+        say(f"qwen8b K=16 verify T={T} mode={mode} seed={seed}")
+        blk = synth.make_block(qwen.cpu, 1, cfg.K, cfg.sigma, T, seed=seed)
+        got, ref = run_verify(qwen, blk, T, mode, seed, 0, ws)
+        compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+        compare_logits(got["logits"], ref["logits"], st)
+    say(f"  {st}")
+    assert st["exact"] >= 2
+
+
+def test_verify_qwen8b_k32_b4(qwen, dev):
+    cfg = synth.CONFIGS["qwen8b_k32_b4"]
+    ws = jsv.new_workspace(qwen.gpu, cfg.batch, cfg.K)
+    st = new_stats()
+    for T in (0.0, 1.0):
+        say(f"qwen8b K=32 B=4 verify T={T}")
+        blk = synth.make_block(qwen.cpu, cfg.batch, cfg.K, cfg.sigma, T, seed=40 + int(T))
+        got, ref = run_verify(qwen, blk, T, SOFT, 5, 9, ws)
+        compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+        compare_logits(got["logits"], ref["logits"], st)
+    say(f"  {st}")
+    assert st["exact"] >= 6
+
+
+def test_verify_d5120(dev):
+    head = synth.head_for(synth.CONFIGS["d5120_k16_b1"])
+    case = Case(head, dev, f64_weight=True)
+    st = new_stats()
+    for name in ("d5120_k16_b1", "d5120_k32_b2"):
+        cfg = synth.CONFIGS[name]
+        ws = jsv.new_workspace(case.gpu, cfg.batch, cfg.K)
+        for T in (0.0, 1.0):
+            say(f"{name} verify T={T}")
+            blk = synth.make_block(head, cfg.batch, cfg.K, cfg.sigma, T, seed=50 + int(T))
+            got, ref = run_verify(case, blk, T, SOFT, 1, 2, ws)
+            compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+            compare_logits(got["logits"], ref["logits"], st)
+    say(f"  {st}")
+    assert st["exact"] >= 4
+
+
+# ---- scoring -----------------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [SOFT, POINT])
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_score_tiny(tiny, dev, mode, T):
+    cfg = synth.CONFIGS["tiny"]
+    ws = jsv.new_workspace(tiny.gpu, 4, cfg.K, 8)
+    st = new_stats()
+    for seed in range(10):
+        say(f"tiny score mode={mode} T={T} seed={seed}")
+        blk = synth.make_block(tiny.cpu, 4, cfg.K, cfg.sigma, T if T > 0 else 1.0, seed=200 + seed)
+        hp = synth.predicted_hidden(blk.hidden, seed)
+        got, ref = run_score(tiny, hp, blk.draft_tokens, blk.draft_logits, T, mode, 8, ws)
+        compare_score(got, ref, st)
+    say(f"  {st}")
+    assert st["exact"] >= 30
+
+
+@pytest.mark.parametrize("mode", [SOFT, POINT])
+def test_score_qwen8b_k16(qwen, dev, mode):
+    cfg = synth.CONFIGS["qwen8b_k16"]
+    ws = jsv.new_workspace(qwen.gpu, 1, cfg.K, 8)
+    st = new_stats()
+    for seed in range(2):
+        say(f"qwen8b score mode={mode} seed={seed}")
+        blk = synth.make_block(qwen.cpu, 1, cfg.K, cfg.sigma, 1.0, seed=seed)
+        hp = synth.predicted_hidden(blk.hidden, seed)
+        got, ref = run_score(qwen, hp, blk.draft_tokens, blk.draft_logits, 1.0, mode, 8, ws)
+        compare_score(got, ref, st)
+    say(f"  {st}")
+    assert st["exact"] >= 1
+
+
+# ---- edge cases ---------------------------------------------------------------------------------
+def test_edge_max_block_ragged_vocab(dev):
+    # B = 8, K = 32: 264 rows in nine passes over a vocabulary that is not a multiple of 16
+    head = synth.random_head(1009, 512, synth.BF16, seed=5)
+    case = Case(head, dev)
+    ws = jsv.new_workspace(case.gpu, 8, 32, 64)
+    st = new_stats()
+    for T in (0.0, 1.0):
+        say(f"edge B=8 K=32 V=1009 T={T}")
+        blk = synth.make_block(head, 8, 32, 0.3, T, seed=77)
+        got, ref = run_verify(case, blk, T, SOFT, 3, 4, ws)
+        compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+        compare_logits(got["logits"], ref["logits"], st)
+        got, ref = run_score(case, blk.hidden, blk.draft_tokens, blk.draft_logits, max(T, 0.7), SOFT, 64, ws)
+        compare_score(got, ref, st)
+    say(f"  {st}")
+
+
+def test_edge_small_vocab_and_k1(dev):
+    head = synth.random_head(10, 256, synth.F32, seed=9)
+    case = Case(head, dev)
+    ws = jsv.new_workspace(case.gpu, 3, 1, 16)
+    st = new_stats()
+    for seed in range(10):
+        T = 1.0 if seed % 2 else 0.0
+        say(f"edge V=10 K=1 seed={seed}")
+        blk = synth.make_block(head, 3, 1, 0.5, T, seed=seed)
+        got, ref = run_verify(case, blk, T, SOFT, seed, 0, ws)
+        compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+        got, ref = run_score(case, blk.hidden, blk.draft_tokens, blk.draft_logits, 1.0, POINT, 16, ws)
+        compare_score(got, ref, st)   # fewer outcomes than top_n: padded
+    say(f"  {st}")
+
+
+def test_edge_invalid_requests(tiny, dev):
+    cfg = synth.CONFIGS["tiny"]
+    ws = jsv.new_workspace(tiny.gpu, 3, cfg.K, 8)
+    blk = synth.make_block(tiny.cpu, 3, cfg.K, cfg.sigma, 1.0, seed=1)
+    blk.hidden[0, 2, 7] = float("nan")            # request 0: non-finite logits
+    blk.draft_tokens[1, 3] = tiny.cpu.vocab        # request 1: draft token out of range
+    st = new_stats()
+    say("edge invalid requests")
+    got, ref = run_verify(tiny, blk, 1.0, SOFT, 0, 0, ws, with_logits=False)
+    assert got["n_accepted"][0] == -1 and got["n_accepted"][1] == -1
+    assert np.all(got["committed"][:2] == -1)
+    assert got["flags"][0] & jsv.FLAG_INVALID and got["flags"][1] & jsv.FLAG_INVALID
+    compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+    got, ref = run_score(tiny, blk.hidden, blk.draft_tokens, blk.draft_logits, 1.0, SOFT, 8, ws)
+    compare_score(got, ref, st)
+    assert st["exact"] >= 2
+
+
+def test_stages_equal_block_and_runs_are_bit_identical(qwen, dev):
+    cfg = synth.CONFIGS["qwen8b_k16"]
+    ws = jsv.new_workspace(qwen.gpu, 1, cfg.K)
+    blk = synth.make_block(qwen.cpu, 1, cfg.K, cfg.sigma, 1.0, seed=123)
+    h, d, g = blk.hidden.to(dev), blk.draft_tokens.to(dev), blk.draft_logits.to(dev)
+    say("stages vs block, bit identity")
+    outs = []
+    for rep in range(3):
+        lo = torch.empty(1, cfg.K + 1, qwen.cpu.vocab, device=dev)
+        o = jsv.verify_block(qwen.gpu, h, d, g, 1.0, SOFT, 9, rep % 2, ws, logits_out=lo)
+        outs.append((o, lo))
+    o2 = jsv.verify_stats(qwen.gpu, h, d, g, 1.0, SOFT, 9, 0, ws)
+    jsv.verify_sample(qwen.gpu, d, g, 1.0, SOFT, ws, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][1], outs[2][1])
+    assert torch.equal(outs[0][0].committed, outs[2][0].committed)
+    assert torch.equal(outs[0][0].committed, o2.committed)
+    assert torch.equal(outs[0][0].n_accepted, o2.n_accepted)
+    assert torch.equal(outs[0][0].flags, o2.flags)

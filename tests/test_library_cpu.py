@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every symbol include/jsverify.h declares, and
+rejects bad arguments on the host with the documented status codes.  No call here
+reaches a kernel launch: every case fails validation first (CPU only)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from draft_block_verification_rmsnorm_amd import jsverify as J
+
+ROOT = Path(__file__).resolve().parents[1]
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails before any use
+
+
+def declared_functions():
+    text = (ROOT / "include" / "jsverify.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(jsv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return J.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("jsv_lmhead_logits", "jsv_verify_block", "jsv_score_outcomes", "jsv_workspace_bytes"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(J.EXPORTED) == set(declared_functions())
+
+
+def test_status_strings_and_version(lib):
+    assert lib.jsv_status_string(0) == b"ok"
+    assert lib.jsv_status_string(-3) == b"workspace too small"
+    assert lib.jsv_version() >= 100
+
+
+def head(vocab=151936, hidden=4096, dtype=J.JSV_BF16, weight=FAKE, norm=FAKE, eps=1e-6):
+    return J._Head(weight, norm, vocab, hidden, eps, dtype)
+
+
+def test_workspace_bytes(lib):
+    h = head()
+    n16 = lib.jsv_workspace_bytes(ctypes.byref(h), 1, 16, 8)
+    n32 = lib.jsv_workspace_bytes(ctypes.byref(h), 4, 32, 8)
+    assert n16 >= 17 * 151936 * 4 and n32 >= 132 * 151936 * 4 and n32 > n16
+    for args in [(0, 16, 8), (9, 16, 8), (1, 0, 8), (1, 33, 8), (1, 16, 65), (1, 16, -1)]:
+        assert lib.jsv_workspace_bytes(ctypes.byref(h), *args) == 0
+    assert lib.jsv_workspace_bytes(None, 1, 16, 8) == 0
+    for bad in [head(hidden=4000), head(hidden=8192 * 2), head(dtype=7), head(vocab=0),
+                head(weight=0), head(weight=FAKE + 8), head(eps=-1.0)]:
+        assert lib.jsv_workspace_bytes(ctypes.byref(bad), 1, 16, 8) == 0
+
+
+def _verify(lib, h=None, **kw):
+    a = dict(hidden=FAKE, drafts=FAKE, dl=FAKE, B=1, K=16, T=1.0, mode=0, seed=0, offset=0,
+             nacc=FAKE, comm=FAKE, flags=0, lout=0, ws=FAKE, wsb=1 << 40, stream=0)
+    a.update(kw)
+    h = h or head()
+    return lib.jsv_verify_block(ctypes.byref(h), a["hidden"], a["drafts"], a["dl"], a["B"], a["K"],
+                                a["T"], a["mode"], a["seed"], a["offset"], a["nacc"], a["comm"],
+                                a["flags"], a["lout"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), J.JSV_EINVAL), (dict(B=9), J.JSV_EINVAL), (dict(K=0), J.JSV_EINVAL),
+    (dict(K=33), J.JSV_EINVAL), (dict(T=-1.0), J.JSV_EINVAL), (dict(T=float("nan")), J.JSV_EINVAL),
+    (dict(T=float("inf")), J.JSV_EINVAL), (dict(mode=2), J.JSV_EINVAL),
+    (dict(hidden=0), J.JSV_EINVAL), (dict(hidden=FAKE + 4), J.JSV_EINVAL),
+    (dict(drafts=0), J.JSV_EINVAL), (dict(nacc=0), J.JSV_EINVAL), (dict(comm=0), J.JSV_EINVAL),
+    (dict(ws=0), J.JSV_EINVAL), (dict(dl=0), J.JSV_EINVAL),            # softmax at T > 0 needs q
+    (dict(wsb=1000), J.JSV_EWORKSPACE),
+])
+def test_verify_argument_errors(lib, kw, code):
+    assert _verify(lib, **kw) == code
+
+
+def test_verify_shape_errors(lib):
+    assert _verify(lib, h=head(hidden=4000)) == J.JSV_EUNSUPPORTED
+    assert _verify(lib, h=head(hidden=256 * 64)) == J.JSV_EUNSUPPORTED
+    assert _verify(lib, h=head(dtype=3)) == J.JSV_EINVAL
+    assert _verify(lib, h=head(vocab=-5)) == J.JSV_EINVAL
+    assert _verify(lib, h=head(vocab=2 ** 31)) == J.JSV_EUNSUPPORTED
+    # the workspace check counts the logits only when the caller gives no logits_out
+    h = head()
+    need = lib.jsv_workspace_bytes(ctypes.byref(h), 1, 16, 0)
+    assert _verify(lib, wsb=need - 1) == J.JSV_EWORKSPACE
+
+
+def test_score_argument_errors(lib):
+    h = head()
+
+    def call(top_n=8, hidden=FAKE, out=FAKE, T=1.0, dl=FAKE, wsb=1 << 40):
+        return lib.jsv_score_outcomes(ctypes.byref(h), hidden, FAKE, dl, 1, 16, T, 0, top_n,
+                                      out, out, out, 0, 0, FAKE, wsb, 0)
+
+    assert call(top_n=0) == J.JSV_EINVAL
+    assert call(top_n=65) == J.JSV_EINVAL
+    assert call(hidden=0) == J.JSV_EINVAL
+    assert call(out=0) == J.JSV_EINVAL
+    assert call(dl=0) == J.JSV_EINVAL
+    assert call(wsb=10) == J.JSV_EWORKSPACE
+
+
+def test_lmhead_argument_errors(lib):
+    h = head()
+    assert lib.jsv_lmhead_logits(ctypes.byref(h), FAKE, -1, FAKE, 0, 0, 0) == J.JSV_EINVAL
+    assert lib.jsv_lmhead_logits(ctypes.byref(h), FAKE, 0, FAKE, 0, 0, 0) == J.JSV_OK  # empty input
+    assert lib.jsv_lmhead_logits(ctypes.byref(h), 0, 4, FAKE, 0, 0, 0) == J.JSV_EINVAL
+    assert lib.jsv_lmhead_logits(ctypes.byref(h), FAKE, 4, 0, 0, 0, 0) == J.JSV_EINVAL
+    bad = head(hidden=100)
+    assert lib.jsv_lmhead_logits(ctypes.byref(bad), FAKE, 4, FAKE, 0, 0, 0) == J.JSV_EUNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        J.load_library(tmp_path / "libjsverify.so")
