@@ -118,15 +118,14 @@ jsv_status run_stats(const StatsCall& c, hipStream_t stream) {
     a.counter = reinterpret_cast<uint32_t*>(c.ws + c.L.counters);
     a.req = reinterpret_cast<ReqState*>(c.ws + c.L.req);
     a.rowfinal = reinterpret_cast<RowFinal*>(c.ws + c.L.rowfinal);
-    a.zd = reinterpret_cast<float*>(c.ws + c.L.zd);
+    a.zd = reinterpret_cast<double*>(c.ws + c.L.zd);
     a.partial = reinterpret_cast<RowStat*>(c.ws + c.L.partial);
   }
   for (int row0 = 0; row0 < c.M; row0 += kRowsPerPass) {
     a.row0 = row0;
     a.rows = (c.M - row0) < kRowsPerPass ? (c.M - row0) : kRowsPerPass;
     a.finalize = (row0 + kRowsPerPass >= c.M) ? c.finalize : kFinalizeNone;
-    const int ntiles = a.rows > 16 ? 2 : 1;
-    if (launch_stats(c.head->dtype, c.nks, ntiles, int(grid), a, stream) != hipSuccess) return JSV_EHIP;
+    if (launch_stats(c.head->dtype, c.nks, a.rows, int(grid), a, stream) != hipSuccess) return JSV_EHIP;
   }
   return JSV_OK;
 }

@@ -11,7 +11,7 @@ namespace jsv {
 constexpr int kWave = 64;
 constexpr int kWaves = 8;                  // waves per workgroup of the LM-head kernel
 constexpr int kThreads = kWaves * kWave;   // 512
-constexpr int kRowsPerPass = 32;           // two 16-token MFMA tiles per pass over W
+constexpr int kRowsPerPass = 33;           // two 16-token MFMA tiles + one VALU row per pass over W
 constexpr int kMaxGrid = 1024;             // LM-head workgroups (= per-row partial records)
 constexpr int kSampleSlices = 64;          // vocabulary slices of the bonus sampler
 constexpr int kScoreSlices = 64;           // vocabulary slices per row of the scorer
@@ -86,7 +86,7 @@ inline WsLayout ws_layout(int64_t V, int B, int K, int top_n) {
   L.counters = off; off = align256(off + kCounterWords * sizeof(uint32_t));
   L.req = off;      off = align256(off + kMaxB * sizeof(ReqState));
   L.rowfinal = off; off = align256(off + M * sizeof(RowFinal));
-  L.zd = off;       off = align256(off + M * sizeof(float));
+  L.zd = off;       off = align256(off + M * sizeof(double));
   L.partial = off;  off = align256(off + size_t(kMaxGrid) * M * sizeof(RowStat));
   const size_t zs_sample = size_t(B) * size_t(sample_slices(V)) * 2 * sizeof(double);
   const size_t zs_score = M * size_t(score_slices(V)) * sizeof(double);
@@ -106,7 +106,7 @@ struct StatsArgs {
   const void* hidden;     // [M][d]
   int64_t V;
   int d;
-  int row0, rows;         // rows handled by this pass (rows <= 32)
+  int row0, rows;         // rows handled by this pass (rows <= kRowsPerPass)
   int M;                  // total rows
   float eps;
   float* logits;          // [M][V]
@@ -117,7 +117,7 @@ struct StatsArgs {
   int stats;              // write per-row partial statistics
   int want_q;             // also draft-logit statistics (softmax proposal, T > 0)
   RowStat* partial;       // [gridDim][M]
-  float* zd;              // [M] logit at the row's draft token
+  double* zd;             // [M] exact logit at the row's draft token (draft rows)
   int finalize;           // FinalizeKind, only on the last pass
   uint32_t* counter;
   int mode;
@@ -173,7 +173,7 @@ struct ScoreArgs {
 // Host-side launchers (jsv_kernels.hip).  Return hipSuccess or the launch error.
 // `nks` is hidden / (kWaves * elements per k-step); the launcher picks the instance.
 bool stats_supported(int dtype, int nks);
-hipError_t launch_stats(int dtype, int nks, int ntiles, int grid, const StatsArgs& a,
+hipError_t launch_stats(int dtype, int nks, int rows, int grid, const StatsArgs& a,
                         hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);

@@ -15,6 +15,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "jsv_internal.h"
 #include "jsverify.h"
 
@@ -22,11 +24,13 @@ namespace jsv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr double kAcceptTie = 1e-4;
 constexpr float kLogitGapTie = 1e-3f;
 constexpr double kCdfTie = 1e-8;
 constexpr double kTopNTie = 1e-3;
+constexpr double kLog2eD = 1.4426950408889634074;
 
 // ------------------------------------------------------------------------------------
 // Philox4x32-10, from the SC'11 paper by Salmon, Moraes, Dror and Shaw.
@@ -211,6 +215,7 @@ __device__ void finalize_block(const StatsArgs& a, int P, Stat* rows_sh) {
   // Phase B: wave b handles request b; lane i handles row i.
   const int K = a.K, R = K + 1;
   const int64_t V = a.V;
+  const double cd = double(kLog2eD) / double(a.T);
   for (int b = w; b < a.B; b += kWaves) {
     const bool act = lane <= K;
     const int row = b * R + lane;
@@ -243,13 +248,15 @@ __device__ void finalize_block(const StatsArgs& a, int P, Stat* rows_sh) {
       // Greedy verification: accept while the draft equals the row's argmax.
       alpha = (lane < K && di == st.idx) ? 1.0 : 0.0;
     } else if (lane < K) {
-      const float zd = a.zd[row];
-      const double pd = double(exp2f((zd - st.m) * c)) / st.s;
+      // p(d) from the float64 logit at the draft token (computed in the prologue), so
+      // that alpha and 1 - alpha keep their digits when alpha is close to 1.
+      const double zd = a.zd[row];
+      const double pd = exp2((zd - double(st.m)) * cd) / st.s;
       if (a.mode == JSV_PROPOSAL_POINT) {
         alpha = pd;
       } else {
-        const float gd = a.G[(size_t)(b * K + lane) * V + di];
-        const double qd = double(exp2f((gd - st.mq) * c)) / st.sq;
+        const double gd = a.G[(size_t)(b * K + lane) * V + di];
+        const double qd = exp2((gd - double(st.mq)) * cd) / st.sq;
         alpha = (pd == 0.0) ? 0.0 : (pd >= qd ? 1.0 : pd / qd);
       }
     }
@@ -312,18 +319,57 @@ __device__ void finalize_block(const StatsArgs& a, int P, Stat* rows_sh) {
   }
 }
 
+// x += W(16 B of one row) . xhat(16 B of one hidden row) on the VALU (rows beyond the
+// MFMA tiles).
+template <int DT>
+__device__ inline float dot16(const uint4& wq, const uint4& xq, float acc) {
+  if constexpr (DT == JSV_BF16) {
+    const uint32_t a[4] = {wq.x, wq.y, wq.z, wq.w};
+    const uint32_t b[4] = {xq.x, xq.y, xq.z, xq.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[e]),
+                                            __builtin_bit_cast(bf16x2, b[e]), acc, false);
+    return acc;
+  } else {
+    acc = fmaf(__uint_as_float(wq.x), __uint_as_float(xq.x), acc);
+    acc = fmaf(__uint_as_float(wq.y), __uint_as_float(xq.y), acc);
+    acc = fmaf(__uint_as_float(wq.z), __uint_as_float(xq.z), acc);
+    acc = fmaf(__uint_as_float(wq.w), __uint_as_float(xq.w), acc);
+    return acc;
+  }
+}
+
+// Prefetch window: the largest divisor of NKS whose W registers fit beside the
+// normalised hidden states (160 of the 256 VGPRs a wave has at 2 waves per SIMD).
+constexpr int pick_window(int NT, int NKS) {
+  for (int D = NKS; D >= 1; --D)
+    if (NKS % D == 0 && NT * NKS * 4 + 4 * D <= 160) return D;
+  return 1;
+}
+
 // ------------------------------------------------------------------------------------
 // Fused RMSNorm + LM head + statistics.  Workgroup wg owns 16-row vocabulary groups
-// [g0, g1); its 8 waves split d into equal k-slices, each wave keeping the normalised
-// hidden states of its slice in registers and streaming the same slice of W straight
-// into MFMA operands, D k-steps ahead.  Per group the 8 partial 16 x (16*NT) tiles are
-// summed through LDS (in fp64, fixed order) and thread (token jj, column ii) folds its
-// logit into running statistics.
-template <int DT, int NT, int NKS, int D>
+// [g0, g1); its 8 waves split d into equal k-slices.  Each wave keeps the normalised
+// hidden states of its slice for the NT full 16-token tiles in registers (MFMA B
+// operand) and streams the same slice of W straight into MFMA A operands, D k-steps
+// ahead; NX further rows (at most one) are dotted on the VALU against a copy of their
+// normalised state in LDS.  Per group the 8 partial tiles are summed through LDS (in
+// fp64, fixed order) and thread (token jj, column ii) folds its logit into running
+// statistics.  The logit at each row's draft token is recomputed exactly (fp64) in the
+// prologue for the acceptance test.
+template <int DT, int NT, int NX, int NKS>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   constexpr int EPL = Elem<DT>::EPL, ESZ = Elem<DT>::ESZ, KS = 4 * EPL;
-  static_assert(D >= 1 && D <= NKS, "prefetch window");
-  __shared__ floatx4 red[2][kWaves][NT][kWave];
+  constexpr int D = pick_window(NT, NKS);
+  constexpr int NTOK = NT * 16 + NX;
+  constexpr int NEP = (NTOK + 31) / 32;   // tokens per epilogue thread
+  constexpr int XLEN = kWaves * NKS * 4;  // 16-byte groups per hidden row
+  constexpr int NT1 = NT > 0 ? NT : 1, NX1 = NX > 0 ? NX : 1;
+  static_assert(NTOK >= 1 && NTOK <= kRowsPerPass && NX <= 1, "tiling");
+  __shared__ floatx4 red[2][kWaves][NT1][kWave];
+  __shared__ float redx[2][kWaves][NX1][16];
+  __shared__ uint4 xrow[NX1][XLEN];
   __shared__ float rnorm[kRowsPerPass];
   __shared__ uint32_t last_flag;
 
@@ -337,141 +383,217 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   const char* Wb = static_cast<const char*>(a.W);
   const int vr = lane & 15;
 
+  // Rows past the vocabulary re-read row V-1: the loads stay branch-free (so the
+  // compiler can keep the whole window in flight) and those output rows are never used.
   auto wload = [&](int64_t g, int s) -> uint4 {
-    const int64_t v = g * 16 + vr;
-    uint4 q = make_uint4(0u, 0u, 0u, 0u);
-    if (v < V) q = *reinterpret_cast<const uint4*>(Wb + ((size_t)v * d + kb + s * KS) * ESZ);
-    return q;
+    int64_t v = g * 16 + vr;
+    v = v < V ? v : V - 1;
+    return *reinterpret_cast<const uint4*>(Wb + ((size_t)v * d + kb + s * KS) * ESZ);
   };
 
   // Start streaming W before the norm prologue.
   uint4 fr[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) fr[j] = (g0 < g1) ? wload(g0, j) : make_uint4(0u, 0u, 0u, 0u);
+  for (int j = 0; j < D; ++j) fr[j] = wload(g0 < g1 ? g0 : 0, j);
 
-  // RMSNorm factors r = 1 / sqrt(mean(h^2) + eps) of the rows of this pass.
+  // RMSNorm factors r = 1 / sqrt(mean(h^2) + eps) of the rows of this pass, in float64
+  // and rounded once to float32: r decides the rounding of every normalised element,
+  // so it is taken at a precision where a different summation order cannot move it.
   const char* Hb = static_cast<const char*>(a.hidden);
+  const char* Gm = static_cast<const char*>(a.gamma);
   for (int r = w; r < a.rows; r += kWaves) {
     const char* hr = Hb + (size_t)(a.row0 + r) * d * ESZ;
-    float ss = 0.f;
+    double ss = 0.0;
     for (int k = lane * EPL; k < d; k += kWave * EPL) {
       float x[EPL];
       unpack<DT>(*reinterpret_cast<const uint4*>(hr + (size_t)k * ESZ), x);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ss = fmaf(x[e], x[e], ss);
+      for (int e = 0; e < EPL; ++e) ss = fma(double(x[e]), double(x[e]), ss);
     }
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if (lane == 0) rnorm[r] = 1.0f / sqrtf(ss / float(d) + a.eps);
+    if (lane == 0) rnorm[r] = float(1.0 / sqrt(ss / double(d) + double(a.eps)));
   }
   __syncthreads();
 
-  // Normalised hidden states of this wave's k-slice, in MFMA B-operand layout.
-  uint4 xf[NT][NKS];
-  const char* Gm = static_cast<const char*>(a.gamma);
+  // Exact (fp64) logit at the draft token of each draft row of this pass: row r is done
+  // by wave (r / P) % 8 of workgroup r % P, overlapping the W stream.
+  if (a.stats && a.K >= 0) {
+    for (int r = wg + P * w; r < a.rows; r += P * kWaves) {
+      const int row = a.row0 + r;
+      const int b = row / (a.K + 1), i = row - b * (a.K + 1);
+      if (i >= a.K) continue;
+      const int dt = a.drafts[b * a.K + i];
+      if (dt < 0 || (int64_t)dt >= V) continue;
+      const char* hr = Hb + (size_t)row * d * ESZ;
+      const char* wr = Wb + (size_t)dt * d * ESZ;
+      double acc = 0.0;
+      for (int k = lane * EPL; k < d; k += kWave * EPL) {
+        const uint4 xq = norm_pack<DT>(*reinterpret_cast<const uint4*>(hr + (size_t)k * ESZ),
+                                       *reinterpret_cast<const uint4*>(Gm + (size_t)k * ESZ), rnorm[r]);
+        float xv[EPL], wv[EPL];
+        unpack<DT>(xq, xv);
+        unpack<DT>(*reinterpret_cast<const uint4*>(wr + (size_t)k * ESZ), wv);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tok = t * 16 + (lane & 15);
-    const bool ok = tok < a.rows;
-    const float r = ok ? rnorm[tok] : 0.f;
-    const char* hr = Hb + (size_t)(a.row0 + (ok ? tok : 0)) * d * ESZ;
+        for (int e = 0; e < EPL; ++e) acc += double(xv[e]) * double(wv[e]);
+      }
+      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      if (lane == 0) a.zd[row] = acc;
+    }
+  }
+
+  // Normalised hidden states of this wave's k-slice for the MFMA tiles.  Padding
+  // tokens read row 0 of the pass with r = 0 (their output columns are never used).
+  uint4 xf[NT1][NKS];
+  {
+    float rt[NT1];
+    const char* hrt[NT1];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int tok = t * 16 + (lane & 15);
+      const bool ok = tok < a.rows;
+      rt[t] = ok ? rnorm[tok] : 0.f;
+      hrt[t] = Hb + (size_t)(a.row0 + (ok ? tok : 0)) * d * ESZ;
+    }
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const int k = kb + s * KS;
-      if (ok) {
-        const uint4 hq = *reinterpret_cast<const uint4*>(hr + (size_t)k * ESZ);
-        const uint4 gq = *reinterpret_cast<const uint4*>(Gm + (size_t)k * ESZ);
-        xf[t][s] = norm_pack<DT>(hq, gq, r);
-      } else {
-        xf[t][s] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      const uint4 gq = *reinterpret_cast<const uint4*>(Gm + (size_t)k * ESZ);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        xf[t][s] = norm_pack<DT>(*reinterpret_cast<const uint4*>(hrt[t] + (size_t)k * ESZ), gq, rt[t]);
+      // keep at most four k-steps of loads in flight here (register pressure)
+      if ((s & 3) == 3) asm volatile("" ::: "memory");
     }
   }
+  // Rows beyond the tiles: whole normalised row in LDS.
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    const int tok = NT * 16 + x;
+    const char* hr = Hb + (size_t)(a.row0 + tok) * d * ESZ;
+    const float r = rnorm[tok];
+    for (int q = tid; q < XLEN; q += kThreads)
+      xrow[x][q] = norm_pack<DT>(*reinterpret_cast<const uint4*>(hr + (size_t)q * 16),
+                                 *reinterpret_cast<const uint4*>(Gm + (size_t)q * 16), r);
+  }
+  if (NX > 0) __syncthreads();
 
-  // Epilogue identity: token jj of this pass, vocabulary column ii of the group.
-  const int jj = tid >> 4, ii = tid & 15;
-  const bool tok_ok = jj < a.rows;
-  const int row = a.row0 + (tok_ok ? jj : 0);
-  bool draft = false;
-  int dtok = -1;
-  const float* grow = nullptr;
-  if (a.K >= 0 && tok_ok) {
-    const int b = row / (a.K + 1), i = row - b * (a.K + 1);
-    draft = i < a.K;
-    if (draft) {
-      dtok = a.drafts[b * a.K + i];
-      if (a.want_q) grow = a.G + (size_t)(b * a.K + i) * V;
-    }
-  }
+  // Epilogue identity: tokens jj = tid/16 (+32), vocabulary column ii of the group.
+  const int ii = tid & 15;
   const bool soft = a.T > 0.f;
   const float c = a.c;
-  Stat st;
-  stat_init(st);
-  float* lrow = a.logits + (size_t)row * V;
+  int jj[NEP], row[NEP];
+  bool tok_ok[NEP];
+  const float* gsrc[NEP];
+  Stat st[NEP];
+#pragma unroll
+  for (int e = 0; e < NEP; ++e) {
+    jj[e] = (tid >> 4) + 32 * e;
+    tok_ok[e] = jj[e] < NTOK && jj[e] < a.rows;
+    row[e] = a.row0 + (tok_ok[e] ? jj[e] : 0);
+    gsrc[e] = nullptr;
+    if (a.want_q && tok_ok[e]) {
+      const int b = row[e] / (a.K + 1), i = row[e] - b * (a.K + 1);
+      if (i < a.K) gsrc[e] = a.G + (size_t)(b * a.K + i) * V;
+    }
+    stat_init(st[e]);
+  }
 
   int buf = 0;
-  for (int64_t g = g0; g < g1; ++g) {
+  // One group: MFMAs over this wave's k-slice, refilling the window from the next group
+  // (REFILL) or only from this one (the last group), then the LDS reduction + epilogue.
+  auto group = [&](int64_t g, auto refill_tag) {
+    constexpr bool REFILL = decltype(refill_tag)::value;
     const int64_t v = g * 16 + ii;
-    float gv = 0.f;
-    const bool gok = grow != nullptr && v < V;
-    if (gok) gv = grow[v];
-    floatx4 acc[NT];
+    const int64_t vc = v < V ? v : V - 1;
+    float gv[NEP];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < NEP; ++e) gv[e] = gsrc[e] ? gsrc[e][vc] : 0.f;
+    floatx4 acc[NT1];
+    float xacc[NX1];
+#pragma unroll
+    for (int t = 0; t < NT1; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < NX1; ++x) xacc[x] = 0.f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const uint4 f = fr[s % D];
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] = mfma_step<DT>(f, xf[t][s], acc[t]);
+#pragma unroll
+      for (int x = 0; x < NX; ++x) xacc[x] = dot16<DT>(f, xrow[x][(kb + s * KS) / EPL], xacc[x]);
       const bool nxt = (s + D) >= NKS;
       const int sn = nxt ? (s + D - NKS) : (s + D);
-      const int64_t gn = g + (nxt ? 1 : 0);
-      if (gn < g1) fr[s % D] = wload(gn, sn);
+      if (!nxt) fr[s % D] = wload(g, sn);
+      else if (REFILL) fr[s % D] = wload(g + 1, sn);
+    }
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      float y = xacc[x];
+      y += __shfl_xor(y, 16);
+      y += __shfl_xor(y, 32);
+      if (lane < 16) redx[buf][w][x][lane] = y;
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) red[buf][w][t][lane] = acc[t];
     __syncthreads();
-    if (jj < NT * 16) {
-      const int t = jj >> 4, src = ((ii >> 2) << 4) + (jj & 15), r = ii & 3;
-      double zz = 0.0;
 #pragma unroll
-      for (int w2 = 0; w2 < kWaves; ++w2) zz += double(red[buf][w2][t][src][r]);
+    for (int e = 0; e < NEP; ++e) {
+      if (jj[e] >= NTOK) continue;
+      double zz = 0.0;
+      if (jj[e] < NT * 16) {
+        const int t = jj[e] >> 4, src = ((ii >> 2) << 4) + (jj[e] & 15), r = ii & 3;
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) zz += double(red[buf][w2][t][src][r]);
+      } else {
+        const int x = jj[e] - NT * 16;
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) zz += double(redx[buf][w2][x][ii]);
+      }
       const float z = float(zz);
-      if (tok_ok && v < V) {
-        lrow[v] = z;
+      if (tok_ok[e] && v < V) {
+        a.logits[(size_t)row[e] * V + v] = z;
         if (a.stats) {
+          Stat& S = st[e];
           if (!(fabsf(z) <= FLT_MAX)) {
-            st.flags |= JSV_FLAG_INVALID;
-          } else if (z > st.m) {
-            if (soft) st.s = st.s * double(exp2f((st.m - z) * c)) + 1.0;
-            st.top2 = st.m; st.m = z; st.idx = int(v);
+            S.flags |= JSV_FLAG_INVALID;
+          } else if (z > S.m) {
+            if (soft) S.s = S.s * double(exp2f((S.m - z) * c)) + 1.0;
+            S.top2 = S.m; S.m = z; S.idx = int(v);
           } else {
-            st.top2 = fmaxf(st.top2, z);
-            if (soft) st.s += double(exp2f((z - st.m) * c));
+            S.top2 = fmaxf(S.top2, z);
+            if (soft) S.s += double(exp2f((z - S.m) * c));
           }
-          if (draft && v == dtok) a.zd[row] = z;
-          if (gok) {
-            if (!(fabsf(gv) <= FLT_MAX)) {
-              st.flags |= JSV_FLAG_INVALID;
-            } else if (gv > st.mq) {
-              st.sq = st.sq * double(exp2f((st.mq - gv) * c)) + 1.0;
-              st.mq = gv;
+          if (gsrc[e] != nullptr) {
+            const float q = gv[e];
+            if (!(fabsf(q) <= FLT_MAX)) {
+              S.flags |= JSV_FLAG_INVALID;
+            } else if (q > S.mq) {
+              S.sq = S.sq * double(exp2f((S.mq - q) * c)) + 1.0;
+              S.mq = q;
             } else {
-              st.sq += double(exp2f((gv - st.mq) * c));
+              S.sq += double(exp2f((q - S.mq) * c));
             }
           }
         }
       }
     }
     buf ^= 1;
+  };
+  if (g0 < g1) {
+    for (int64_t g = g0; g + 1 < g1; ++g) group(g, std::true_type{});
+    group(g1 - 1, std::false_type{});
   }
 
   if (!a.stats) return;
-  for (int off = 1; off < 16; off <<= 1) stat_merge(st, stat_shfl_xor(st, off), c, soft);
-  if (ii == 0 && tok_ok) {
-    RowStat rs{};
-    rs.s = st.s; rs.sq = st.sq; rs.m = st.m; rs.top2 = st.top2; rs.mq = st.mq;
-    rs.idx = st.idx; rs.flags = st.flags;
-    a.partial[(size_t)wg * a.M + row] = rs;
+#pragma unroll
+  for (int e = 0; e < NEP; ++e) {
+    for (int off = 1; off < 16; off <<= 1) stat_merge(st[e], stat_shfl_xor(st[e], off), c, soft);
+    if (ii == 0 && tok_ok[e]) {
+      RowStat rs{};
+      rs.s = st[e].s; rs.sq = st[e].sq; rs.m = st[e].m; rs.top2 = st[e].top2; rs.mq = st[e].mq;
+      rs.idx = st[e].idx; rs.flags = st[e].flags;
+      a.partial[(size_t)wg * a.M + row[e]] = rs;
+    }
   }
   if (a.finalize == kFinalizeNone) return;
 
@@ -612,30 +734,42 @@ __global__ __launch_bounds__(kSliceThreads) void sample_kernel(SampleArgs a) {
   __threadfence();
 
   uint32_t f = 0;
-  if (tid == 0) {
-    const double* zs = a.zs + (size_t)b * NB * 2;
-    double Zr = 0.0, Zp = 0.0;
-    for (int q = 0; q < NB; ++q) { Zr += zs[2 * q]; Zp += zs[2 * q + 1]; }
+  {
+    // Locate the slice holding t = v_k * Z: block sums and an exclusive scan over the
+    // slice totals (each thread owns a contiguous run of slices), then the first slice
+    // whose cumulative mass exceeds t.
+    const double* zsb = a.zs + (size_t)b * NB * 2;
+    const int SE = (NB + kSliceThreads - 1) / kSliceThreads;
+    const int q0 = tid * SE, q1 = min(NB, q0 + SE);
+    double xr = 0.0, xp = 0.0;
+    for (int q = q0; q < q1; ++q) { xr += zsb[2 * q]; xp += zsb[2 * q + 1]; }
+    const double Zr = block_sum(xr, dsh);
+    const double Zp = block_sum(xp, dsh);
     const int zero = (Zr > 0.0) ? 0 : 1;
     const double Z = zero ? Zp : Zr;
     const double t = rq.vk * Z;
-    double cum = 0.0, base = 0.0;
-    int s = -1, last_nz = 0;
-    for (int q = 0; q < NB; ++q) {
-      const double x = zs[2 * q + zero];
-      if (x > 0.0) last_nz = q;
-      if (s < 0 && x > 0.0 && cum + x > t) { s = q; base = cum; }
-      cum += x;
+    double cb = block_exclusive_scan(zero ? xp : xr, dsh);
+    int cand = INT_MAX, lastnz = -1;
+    double cbase = 0.0;
+    for (int q = q0; q < q1; ++q) {
+      const double x = zsb[2 * q + zero];
+      if (x > 0.0) lastnz = q;
+      if (cand == INT_MAX && x > 0.0 && cb + x > t) { cand = q; cbase = cb; }
+      cb += x;
     }
-    int fall = 0;
-    if (s < 0) {  // rounding left t at or above the last CDF value
-      s = last_nz;
-      fall = 1;
-      double c2 = 0.0;
-      for (int q = 0; q < s; ++q) c2 += zs[2 * q + zero];
-      base = c2;
+    const int sfound = block_min_int(cand, ish);
+    const int slast = block_max_int(lastnz, ish);
+    if (sfound != INT_MAX && cand == sfound) bc_base = cbase;
+    if (sfound == INT_MAX) {  // rounding left t at or above the last CDF value
+      double c2 = block_exclusive_scan(zero ? xp : xr, dsh);
+      for (int q = q0; q < q1 && q < slast; ++q) c2 += zsb[2 * q + zero];
+      if (q0 <= slast && slast < q1) bc_base = c2;
     }
-    bc_t = t; bc_base = base; bc_Z = Z; bc_s = s; bc_zero = zero; bc_fall = fall;
+    if (tid == 0) {
+      bc_t = t; bc_Z = Z; bc_zero = zero;
+      bc_s = (sfound != INT_MAX) ? sfound : (slast >= 0 ? slast : 0);
+      bc_fall = (sfound == INT_MAX) ? 1 : 0;
+    }
   }
   __syncthreads();
   const int s = bc_s, zero = bc_zero;
@@ -784,15 +918,27 @@ __global__ __launch_bounds__(kSliceThreads) void score_kernel(ScoreArgs a) {
 
   // Merge: scale_k turns a candidate of row k into P(k, a).
   __shared__ double scale_sh[kMaxK + 1];
+  __shared__ double zk_sh[kMaxK + 1];
   __shared__ int usep_sh[kMaxK + 1];
   __shared__ uint32_t flag_sh;
   if (tid == 0) flag_sh = 0u;
   __syncthreads();
+  // Residual mass of row kk: wave kk % 4 sums its slice totals (fixed order per lane,
+  // then a fixed shuffle tree).
+  {
+    const int w = tid >> 6, lane = tid & 63;
+    for (int kk = w; kk < R; kk += kSliceThreads / kWave) {
+      double x = 0.0;
+      for (int q = lane; q < NB; q += kWave) x += a.zs[((size_t)(b * R + kk)) * NB + q];
+      for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+      if (lane == 0) zk_sh[kk] = x;
+    }
+  }
+  __syncthreads();
   for (int kk = tid; kk < R; kk += kSliceThreads) {
     const RowFinal f2 = a.rowfinal[b * R + kk];
     const double P2 = (kk < K) ? f2.A * (1.0 - f2.alpha) : f2.A;
-    double Zk = 0.0;
-    for (int q = 0; q < NB; ++q) Zk += a.zs[((size_t)(b * R + kk)) * NB + q];
+    const double Zk = zk_sh[kk];
     double sc = 0.0;
     int usep = 0;
     if (P2 > 0.0) {
@@ -844,15 +990,9 @@ __global__ __launch_bounds__(kSliceThreads) void score_kernel(ScoreArgs a) {
 
 // ------------------------------------------------------------------------------------
 // Launchers.
-template <int DT, int NT, int NKS>
+template <int DT, int NT, int NX, int NKS>
 static hipError_t launch_stats_t(int grid, const StatsArgs& a, hipStream_t stream) {
-  // Prefetch window: the largest of a whole, half or quarter group whose W registers fit
-  // beside the normalised hidden states (192 of the 256 VGPRs at 2 waves per SIMD).
-  constexpr int XR = NT * NKS * 4;
-  constexpr int D = (XR + NKS * 4 <= 192) ? NKS
-                  : (XR + (NKS / 2) * 4 <= 192 && NKS >= 2) ? NKS / 2
-                  : (NKS >= 4 ? NKS / 4 : 1);
-  hipLaunchKernelGGL((stats_kernel<DT, NT, NKS, D>), dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((stats_kernel<DT, NT, NX, NKS>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -868,24 +1008,32 @@ bool stats_supported(int dtype, int nks) {
   }
 }
 
-template <int DT, int NT>
+template <int DT, int NT, int NX>
 static hipError_t dispatch_nks(int nks, int grid, const StatsArgs& a, hipStream_t s) {
   switch (nks) {
-#define JSV_CASE(n) case n: return launch_stats_t<DT, NT, n>(grid, a, s);
+#define JSV_CASE(n) case n: return launch_stats_t<DT, NT, NX, n>(grid, a, s);
     JSV_NKS_LIST(JSV_CASE)
 #undef JSV_CASE
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_stats(int dtype, int nks, int ntiles, int grid, const StatsArgs& a,
+// Tiling of `rows` (1..33) tokens: full 16-token MFMA tiles, and one leftover row on
+// the VALU when exactly one row is left over.
+template <int DT>
+static hipError_t dispatch_rows(int rows, int nks, int grid, const StatsArgs& a, hipStream_t s) {
+  if (rows <= 1) return dispatch_nks<DT, 0, 1>(nks, grid, a, s);
+  if (rows <= 16) return dispatch_nks<DT, 1, 0>(nks, grid, a, s);
+  if (rows == 17) return dispatch_nks<DT, 1, 1>(nks, grid, a, s);
+  if (rows <= 32) return dispatch_nks<DT, 2, 0>(nks, grid, a, s);
+  return dispatch_nks<DT, 2, 1>(nks, grid, a, s);
+}
+
+hipError_t launch_stats(int dtype, int nks, int rows, int grid, const StatsArgs& a,
                         hipStream_t stream) {
-  if (dtype == JSV_BF16) {
-    return ntiles == 1 ? dispatch_nks<JSV_BF16, 1>(nks, grid, a, stream)
-                       : dispatch_nks<JSV_BF16, 2>(nks, grid, a, stream);
-  }
-  return ntiles == 1 ? dispatch_nks<JSV_F32, 1>(nks, grid, a, stream)
-                     : dispatch_nks<JSV_F32, 2>(nks, grid, a, stream);
+  if (rows < 1 || rows > kRowsPerPass) return hipErrorInvalidValue;
+  return dtype == JSV_BF16 ? dispatch_rows<JSV_BF16>(rows, nks, grid, a, stream)
+                           : dispatch_rows<JSV_F32>(rows, nks, grid, a, stream);
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {

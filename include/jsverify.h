@@ -89,7 +89,8 @@ typedef struct {
 size_t jsv_workspace_bytes(const jsv_lm_head* head, int32_t batch, int32_t K, int32_t top_n);
 
 /* Final RMSNorm then LM head for `rows` hidden states (paper §4.2 "Decoder"):
-     x = round_dtype( fp32( fp32(h * r) * gamma ) ),  r = 1 / sqrt(mean(h^2) + eps)
+     x = round_dtype( fp32( fp32(h * r) * gamma ) ),
+     r = fp32( 1 / sqrt(mean(h^2) + eps) )   (evaluated in float64, rounded once)
      logits[m][v] = sum_j x[m][j] * W[v][j]  (fp32 accumulate)
    hidden: device [rows][hidden] in `dtype`; logits: device [rows][vocab] fp32.       */
 jsv_status jsv_lmhead_logits(const jsv_lm_head* head, const void* hidden, int64_t rows,
