@@ -83,7 +83,7 @@ def main():
         jsv.verify_stats(head, hidden, drafts, G, T, mode, 1234, i, ws, out=out, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        jsv.verify_sample(head, drafts, G, T, mode, ws, out, stream=stream)
+        jsv.verify_sample(head, hidden, drafts, G, T, mode, 1234, i, ws, out=out, stream=stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -130,10 +130,10 @@ def main():
                    "temperature": T},
         "latency_ms": {"call_median": round(call[len(call) // 2], 4),
                        "call_p90": round(call[int(0.9 * (len(call) - 1))], 4),
-                       "stats_kernel_mean": round(k1_ms, 4), "sample_kernel_mean": round(mean(k2), 4)},
+                       "stats_kernel_mean": round(k1_ms, 4), "accept_and_bonus_mean": round(mean(k2), 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "stats_kernel (fused RMSNorm + LM head + softmax statistics + acceptance scan)",
+                     "kernel": "stats_kernel (fused RMSNorm + LM head + softmax statistics)",
                      "algorithmic_bytes": abytes},
         "accepted_last_step": n_acc,
     }

@@ -36,7 +36,7 @@ jsv_status check_head(const jsv_lm_head* h, int* nks) {
   if (h->vocab < 1 || h->hidden < 1) return JSV_EINVAL;
   if (!(h->eps >= 0.f) || !isfinite(h->eps)) return JSV_EINVAL;
   if (!aligned16(h->weight) || !aligned16(h->norm_weight)) return JSV_EINVAL;
-  if (h->vocab > INT32_MAX) return JSV_EUNSUPPORTED;
+  if (h->vocab > kMaxVocab) return JSV_EUNSUPPORTED;
   const int64_t step = int64_t(kWaves) * k_per_step(h->dtype);
   if (h->hidden % step != 0) return JSV_EUNSUPPORTED;
   const int64_t n = h->hidden / step;
@@ -52,82 +52,70 @@ jsv_status check_block(int32_t B, int32_t K, float T, int32_t mode) {
   return JSV_OK;
 }
 
-struct StatsCall {
-  const jsv_lm_head* head;
-  int nks;
-  const void* hidden;
-  int M;
-  float* logits;
-  const float* G;
-  const int32_t* drafts;
-  int B, K;
-  float T;
-  int mode;
-  int stats;
-  int finalize;
-  uint64_t seed, offset;
-  int32_t* n_accepted;
-  int32_t* committed;
-  uint32_t* flags;
-  int top_n;
-  int32_t* out_len;
-  int32_t* out_token;
-  float* out_prob;
-  double* len_marginal;
-  char* ws;
-  WsLayout L;
-};
-
-jsv_status run_stats(const StatsCall& c, hipStream_t stream) {
-  const int64_t V = c.head->vocab;
-  const int64_t ngroups = (V + 15) / 16;
+// Workgroups of the LM-head kernel: one per CU, at most one per 16-row vocabulary group.
+int stats_grid(int64_t V) {
   const int cus = device_cu_count();
-  if (cus <= 0) return JSV_EHIP;
+  if (cus <= 0) return 0;
   int64_t grid = cus < kMaxGrid ? cus : kMaxGrid;
-  if (grid > ngroups) grid = ngroups;
+  const int64_t ngroups = (V + 15) / 16;
+  return int(grid > ngroups ? ngroups : grid);
+}
 
+// One or more passes of the LM-head kernel over W, kRowsPerPass rows each.
+jsv_status run_stats(const jsv_lm_head* head, int nks, const void* hidden, int M, float* logits,
+                     const float* G, int B, int K, float T, int mode, int stats, RowStat* partial,
+                     float* rnorm, hipStream_t stream) {
+  const int grid = stats_grid(head->vocab);
+  if (grid <= 0) return JSV_EHIP;
   StatsArgs a{};
-  a.W = c.head->weight;
-  a.gamma = c.head->norm_weight;
-  a.hidden = c.hidden;
-  a.V = V;
-  a.d = int(c.head->hidden);
-  a.M = c.M;
-  a.eps = c.head->eps;
-  a.logits = c.logits;
-  a.G = c.G;
-  a.drafts = c.drafts;
-  a.B = c.B;
-  a.K = c.K;
-  a.T = c.T;
-  a.c = c.T > 0.f ? kLog2e / c.T : 0.f;
-  a.stats = c.stats;
-  a.want_q = (c.stats && c.mode == JSV_PROPOSAL_SOFTMAX && c.T > 0.f && c.G != nullptr) ? 1 : 0;
-  a.mode = c.mode;
-  a.seed = c.seed;
-  a.offset = c.offset;
-  a.n_accepted = c.n_accepted;
-  a.committed = c.committed;
-  a.flags = c.flags;
-  a.top_n = c.top_n;
-  a.out_len = c.out_len;
-  a.out_token = c.out_token;
-  a.out_prob = c.out_prob;
-  a.len_marginal = c.len_marginal;
-  if (c.ws != nullptr) {
-    a.counter = reinterpret_cast<uint32_t*>(c.ws + c.L.counters);
-    a.req = reinterpret_cast<ReqState*>(c.ws + c.L.req);
-    a.rowfinal = reinterpret_cast<RowFinal*>(c.ws + c.L.rowfinal);
-    a.zd = reinterpret_cast<double*>(c.ws + c.L.zd);
-    a.partial = reinterpret_cast<RowStat*>(c.ws + c.L.partial);
-  }
-  for (int row0 = 0; row0 < c.M; row0 += kRowsPerPass) {
+  a.W = head->weight;
+  a.gamma = head->norm_weight;
+  a.hidden = hidden;
+  a.V = head->vocab;
+  a.d = int(head->hidden);
+  a.M = M;
+  a.eps = head->eps;
+  a.logits = logits;
+  a.G = G;
+  a.B = B;
+  a.K = K;
+  a.T = T;
+  a.c = T > 0.f ? kLog2e / T : 0.f;
+  a.stats = stats;
+  a.want_q = (stats && mode == JSV_PROPOSAL_SOFTMAX && T > 0.f && G != nullptr) ? 1 : 0;
+  a.partial = partial;
+  a.rnorm = rnorm;
+  for (int row0 = 0; row0 < M; row0 += kRowsPerPass) {
     a.row0 = row0;
-    a.rows = (c.M - row0) < kRowsPerPass ? (c.M - row0) : kRowsPerPass;
-    a.finalize = (row0 + kRowsPerPass >= c.M) ? c.finalize : kFinalizeNone;
-    if (launch_stats(c.head->dtype, c.nks, a.rows, int(grid), a, stream) != hipSuccess) return JSV_EHIP;
+    a.rows = (M - row0) < kRowsPerPass ? (M - row0) : kRowsPerPass;
+    if (launch_stats(head->dtype, nks, grid, a, stream) != hipSuccess) return JSV_EHIP;
   }
   return JSV_OK;
+}
+
+FinalArgs final_args(const jsv_lm_head* head, const void* hidden, const int32_t* drafts,
+                     const float* G, int B, int K, float T, int mode, int kind, char* ws,
+                     const WsLayout& L) {
+  FinalArgs f{};
+  f.W = head->weight;
+  f.gamma = head->norm_weight;
+  f.hidden = hidden;
+  f.V = head->vocab;
+  f.d = int(head->hidden);
+  f.dtype = head->dtype;
+  f.G = G;
+  f.drafts = drafts;
+  f.B = B;
+  f.K = K;
+  f.T = T;
+  f.mode = mode;
+  f.kind = kind;
+  f.P = stats_grid(head->vocab);
+  f.partial = reinterpret_cast<const RowStat*>(ws + L.partial);
+  f.rnorm = reinterpret_cast<const float*>(ws + L.rnorm);
+  f.rowfinal = reinterpret_cast<RowFinal*>(ws + L.rowfinal);
+  f.req = reinterpret_cast<ReqState*>(ws + L.req);
+  return f;
 }
 
 size_t needed_bytes(int64_t V, int B, int K, int top_n, bool logits_in_ws) {
@@ -171,24 +159,22 @@ jsv_status jsv_lmhead_logits(const jsv_lm_head* head, const void* hidden, int64_
   if (hidden == nullptr || logits == nullptr || !aligned16(hidden)) return JSV_EINVAL;
   if (rows > INT32_MAX / 2) return JSV_EUNSUPPORTED;
   (void)hipGetLastError();
-  StatsCall c{};
-  c.head = head; c.nks = nks; c.hidden = hidden; c.M = int(rows); c.logits = logits;
-  c.K = -1; c.B = 0; c.T = 0.f; c.stats = 0; c.finalize = kFinalizeNone; c.ws = nullptr;
-  return run_stats(c, static_cast<hipStream_t>(hip_stream));
+  return run_stats(head, nks, hidden, int(rows), logits, nullptr, 0, -1, 0.f, JSV_PROPOSAL_POINT,
+                   0, nullptr, nullptr, static_cast<hipStream_t>(hip_stream));
 }
 
 static jsv_status verify_prepare(const jsv_lm_head* head, const void* hidden,
                                  const int32_t* draft_tokens, const float* draft_logits,
                                  int32_t B, int32_t K, float T, int32_t mode, int32_t* n_accepted,
                                  int32_t* committed, const float* logits_out, void* ws,
-                                 size_t ws_bytes, int* nks, bool need_hidden) {
+                                 size_t ws_bytes, int* nks) {
   jsv_status st = check_head(head, nks);
   if (st != JSV_OK) return st;
   st = check_block(B, K, T, mode);
   if (st != JSV_OK) return st;
-  if (need_hidden && (hidden == nullptr || !aligned16(hidden))) return JSV_EINVAL;
+  if (hidden == nullptr || !aligned16(hidden)) return JSV_EINVAL;
   if (draft_tokens == nullptr || committed == nullptr || ws == nullptr) return JSV_EINVAL;
-  if (need_hidden && n_accepted == nullptr) return JSV_EINVAL;
+  if (n_accepted == nullptr) return JSV_EINVAL;
   if (mode == JSV_PROPOSAL_SOFTMAX && T > 0.f && draft_logits == nullptr) return JSV_EINVAL;
   if (!aligned16(ws)) return JSV_EINVAL;
   if (ws_bytes < needed_bytes(head->vocab, B, K, 0, logits_out == nullptr)) return JSV_EWORKSPACE;
@@ -201,35 +187,45 @@ jsv_status jsv_verify_stats(const jsv_lm_head* head, const void* hidden,
                             uint64_t offset, int32_t* n_accepted, int32_t* committed,
                             uint32_t* flags, float* logits_out, void* ws, size_t ws_bytes,
                             void* hip_stream) {
+  (void)seed;
+  (void)offset;
+  (void)flags;
   int nks = 0;
   jsv_status st = verify_prepare(head, hidden, draft_tokens, draft_logits, B, K, temperature, mode,
-                                 n_accepted, committed, logits_out, ws, ws_bytes, &nks, true);
+                                 n_accepted, committed, logits_out, ws, ws_bytes, &nks);
   if (st != JSV_OK) return st;
-  (void)hipGetLastError();
-  StatsCall c{};
-  c.head = head; c.nks = nks; c.hidden = hidden; c.M = B * (K + 1);
-  c.L = ws_layout(head->vocab, B, K, 0);
-  c.ws = static_cast<char*>(ws);
-  c.logits = logits_out ? logits_out : reinterpret_cast<float*>(c.ws + c.L.logits);
-  c.G = draft_logits; c.drafts = draft_tokens; c.B = B; c.K = K; c.T = temperature; c.mode = mode;
-  c.stats = 1; c.finalize = kFinalizeVerify; c.seed = seed; c.offset = offset;
-  c.n_accepted = n_accepted; c.committed = committed; c.flags = flags;
-  return run_stats(c, static_cast<hipStream_t>(hip_stream));
-}
-
-jsv_status jsv_verify_sample(const jsv_lm_head* head, const int32_t* draft_tokens,
-                             const float* draft_logits, int32_t B, int32_t K, float temperature,
-                             int32_t mode, int32_t* committed, uint32_t* flags,
-                             const float* logits_out, void* ws, size_t ws_bytes,
-                             void* hip_stream) {
-  int nks = 0;
-  jsv_status st = verify_prepare(head, nullptr, draft_tokens, draft_logits, B, K, temperature, mode,
-                                 nullptr, committed, logits_out, ws, ws_bytes, &nks, false);
-  if (st != JSV_OK) return st;
-  if (!(temperature > 0.f)) return JSV_OK;  // greedy: the bonus is the argmax, already written
   (void)hipGetLastError();
   const WsLayout L = ws_layout(head->vocab, B, K, 0);
   char* w = static_cast<char*>(ws);
+  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(w + L.logits);
+  return run_stats(head, nks, hidden, B * (K + 1), logits, draft_logits, B, K, temperature, mode, 1,
+                   reinterpret_cast<RowStat*>(w + L.partial), reinterpret_cast<float*>(w + L.rnorm),
+                   static_cast<hipStream_t>(hip_stream));
+}
+
+jsv_status jsv_verify_sample(const jsv_lm_head* head, const void* hidden,
+                             const int32_t* draft_tokens, const float* draft_logits, int32_t B,
+                             int32_t K, float temperature, int32_t mode, uint64_t seed,
+                             uint64_t offset, int32_t* n_accepted, int32_t* committed,
+                             uint32_t* flags, const float* logits_out, void* ws, size_t ws_bytes,
+                             void* hip_stream) {
+  int nks = 0;
+  jsv_status st = verify_prepare(head, hidden, draft_tokens, draft_logits, B, K, temperature, mode,
+                                 n_accepted, committed, logits_out, ws, ws_bytes, &nks);
+  if (st != JSV_OK) return st;
+  (void)hipGetLastError();
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const WsLayout L = ws_layout(head->vocab, B, K, 0);
+  char* w = static_cast<char*>(ws);
+  FinalArgs f = final_args(head, hidden, draft_tokens, draft_logits, B, K, temperature, mode,
+                           kFinalizeVerify, w, L);
+  f.seed = seed;
+  f.offset = offset;
+  f.n_accepted = n_accepted;
+  f.committed = committed;
+  f.flags = flags;
+  if (f.P <= 0 || launch_finalize(f, stream) != hipSuccess) return JSV_EHIP;
+  if (!(temperature > 0.f)) return JSV_OK;  // greedy: the bonus is the argmax, already written
   SampleArgs a{};
   a.V = head->vocab;
   a.B = B;
@@ -243,10 +239,9 @@ jsv_status jsv_verify_sample(const jsv_lm_head* head, const int32_t* draft_token
   a.rowfinal = reinterpret_cast<const RowFinal*>(w + L.rowfinal);
   a.req = reinterpret_cast<const ReqState*>(w + L.req);
   a.zs = reinterpret_cast<double*>(w + L.zs);
-  a.counter = reinterpret_cast<uint32_t*>(w + L.counters) + 8;
   a.committed = committed;
   a.flags = flags;
-  return launch_sample(a, static_cast<hipStream_t>(hip_stream)) == hipSuccess ? JSV_OK : JSV_EHIP;
+  return launch_sample(a, stream) == hipSuccess ? JSV_OK : JSV_EHIP;
 }
 
 jsv_status jsv_verify_block(const jsv_lm_head* head, const void* hidden,
@@ -259,8 +254,9 @@ jsv_status jsv_verify_block(const jsv_lm_head* head, const void* hidden,
                                    mode, seed, offset, n_accepted, committed, flags, logits_out,
                                    ws, ws_bytes, hip_stream);
   if (st != JSV_OK) return st;
-  return jsv_verify_sample(head, draft_tokens, draft_logits, B, K, temperature, mode, committed,
-                           flags, logits_out, ws, ws_bytes, hip_stream);
+  return jsv_verify_sample(head, hidden, draft_tokens, draft_logits, B, K, temperature, mode, seed,
+                           offset, n_accepted, committed, flags, logits_out, ws, ws_bytes,
+                           hip_stream);
 }
 
 jsv_status jsv_score_outcomes(const jsv_lm_head* head, const void* hidden_pred,
@@ -282,17 +278,23 @@ jsv_status jsv_score_outcomes(const jsv_lm_head* head, const void* hidden_pred,
   if (ws_bytes < needed_bytes(head->vocab, B, K, top_n, true)) return JSV_EWORKSPACE;
   (void)hipGetLastError();
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  StatsCall c{};
-  c.head = head; c.nks = nks; c.hidden = hidden_pred; c.M = B * (K + 1);
-  c.L = ws_layout(head->vocab, B, K, top_n);
-  c.ws = static_cast<char*>(ws);
-  c.logits = reinterpret_cast<float*>(c.ws + c.L.logits);
-  c.G = draft_logits; c.drafts = draft_tokens; c.B = B; c.K = K; c.T = temperature; c.mode = mode;
-  c.stats = 1; c.finalize = kFinalizeScore;
-  c.flags = flags; c.top_n = top_n; c.out_len = out_len; c.out_token = out_token;
-  c.out_prob = out_prob; c.len_marginal = len_marginal;
-  st = run_stats(c, stream);
-  if (st != JSV_OK || !(temperature > 0.f)) return st;
+  const WsLayout L = ws_layout(head->vocab, B, K, top_n);
+  char* w = static_cast<char*>(ws);
+  float* logits = reinterpret_cast<float*>(w + L.logits);
+  st = run_stats(head, nks, hidden_pred, B * (K + 1), logits, draft_logits, B, K, temperature, mode,
+                 1, reinterpret_cast<RowStat*>(w + L.partial), reinterpret_cast<float*>(w + L.rnorm),
+                 stream);
+  if (st != JSV_OK) return st;
+  FinalArgs f = final_args(head, hidden_pred, draft_tokens, draft_logits, B, K, temperature, mode,
+                           kFinalizeScore, w, L);
+  f.flags = flags;
+  f.top_n = top_n;
+  f.out_len = out_len;
+  f.out_token = out_token;
+  f.out_prob = out_prob;
+  f.len_marginal = len_marginal;
+  if (f.P <= 0 || launch_finalize(f, stream) != hipSuccess) return JSV_EHIP;
+  if (!(temperature > 0.f)) return JSV_OK;
   ScoreArgs a{};
   a.V = head->vocab;
   a.B = B;
@@ -301,14 +303,13 @@ jsv_status jsv_score_outcomes(const jsv_lm_head* head, const void* hidden_pred,
   a.c = kLog2e / temperature;
   a.mode = mode;
   a.top_n = top_n;
-  a.logits = c.logits;
+  a.logits = logits;
   a.G = draft_logits;
   a.drafts = draft_tokens;
-  a.rowfinal = reinterpret_cast<const RowFinal*>(c.ws + c.L.rowfinal);
-  a.req = reinterpret_cast<const ReqState*>(c.ws + c.L.req);
-  a.zs = reinterpret_cast<double*>(c.ws + c.L.zs);
-  a.cand = reinterpret_cast<Cand*>(c.ws + c.L.cand);
-  a.counter = reinterpret_cast<uint32_t*>(c.ws + c.L.counters) + 16;
+  a.rowfinal = reinterpret_cast<const RowFinal*>(w + L.rowfinal);
+  a.req = reinterpret_cast<const ReqState*>(w + L.req);
+  a.zs = reinterpret_cast<double*>(w + L.zs);
+  a.cand = reinterpret_cast<Cand*>(w + L.cand);
   a.out_len = out_len;
   a.out_token = out_token;
   a.out_prob = out_prob;

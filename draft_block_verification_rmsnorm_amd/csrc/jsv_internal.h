@@ -12,14 +12,16 @@ constexpr int kWave = 64;
 constexpr int kWaves = 8;                  // waves per workgroup of the LM-head kernel
 constexpr int kThreads = kWaves * kWave;   // 512
 constexpr int kRowsPerPass = 33;           // two 16-token MFMA tiles + one VALU row per pass over W
-constexpr int kMaxGrid = 1024;             // LM-head workgroups (= per-row partial records)
+constexpr int kMaxGrid = 1024;             // LM-head workgroups (= partial records per row)
 constexpr int kSampleSlices = 64;          // vocabulary slices of the bonus sampler
 constexpr int kScoreSlices = 64;           // vocabulary slices per row of the scorer
 constexpr int kSliceThreads = 256;
 constexpr int kMaxB = 8;
 constexpr int kMaxK = 32;
 constexpr int kMaxTopN = 64;
-constexpr int kCounterWords = 64;          // [0] LM-head arrivals, [8+b] sampler, [16+b] scorer
+constexpr int kSampleMaxSlice = 4096;      // columns staged in LDS by one sampler workgroup
+constexpr int kScoreMaxSlice = 2048;       // columns staged in LDS by one scorer workgroup
+constexpr int64_t kMaxVocab = int64_t(1) << 22;
 
 // Per (LM-head workgroup, row) partial statistics of the logits and draft logits.
 struct alignas(16) RowStat {
@@ -44,7 +46,7 @@ struct alignas(16) RowFinal {
   int pad[3];
 };
 
-// Per-request result of the acceptance scan, read by the bonus sampler.
+// Per-request result of the acceptance scan, read by the bonus sampler and scorer.
 struct alignas(16) ReqState {
   double vk;       // bonus uniform of row k
   int k;           // first rejection (K if none); -1 for an invalid request
@@ -60,20 +62,17 @@ struct alignas(8) Cand {
   int pad;
 };
 
-constexpr int kSampleMaxSlice = 4096;      // columns staged in LDS by one sampler workgroup
-constexpr int kScoreMaxSlice = 2048;       // columns staged in LDS by one scorer workgroup
-
-inline int sample_slices(int64_t V) {
+__host__ __device__ inline int sample_slices(int64_t V) {
   const int64_t need = (V + kSampleMaxSlice - 1) / kSampleMaxSlice;
   return int(need > kSampleSlices ? need : kSampleSlices);
 }
-inline int score_slices(int64_t V) {
+__host__ __device__ inline int score_slices(int64_t V) {
   const int64_t need = (V + kScoreMaxSlice - 1) / kScoreMaxSlice;
   return int(need > kScoreSlices ? need : kScoreSlices);
 }
 
 struct WsLayout {
-  size_t counters, req, rowfinal, zd, partial, zs, cand, logits, total;
+  size_t req, rowfinal, rnorm, partial, zs, cand, logits, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -83,10 +82,9 @@ inline WsLayout ws_layout(int64_t V, int B, int K, int top_n) {
   const size_t M = size_t(B) * size_t(K + 1);
   WsLayout L{};
   size_t off = 0;
-  L.counters = off; off = align256(off + kCounterWords * sizeof(uint32_t));
   L.req = off;      off = align256(off + kMaxB * sizeof(ReqState));
   L.rowfinal = off; off = align256(off + M * sizeof(RowFinal));
-  L.zd = off;       off = align256(off + M * sizeof(double));
+  L.rnorm = off;    off = align256(off + M * sizeof(float));
   L.partial = off;  off = align256(off + size_t(kMaxGrid) * M * sizeof(RowStat));
   const size_t zs_sample = size_t(B) * size_t(sample_slices(V)) * 2 * sizeof(double);
   const size_t zs_score = M * size_t(score_slices(V)) * sizeof(double);
@@ -97,9 +95,7 @@ inline WsLayout ws_layout(int64_t V, int B, int K, int top_n) {
   return L;
 }
 
-enum FinalizeKind { kFinalizeNone = 0, kFinalizeVerify = 1, kFinalizeScore = 2 };
-
-// Arguments of the fused RMSNorm + LM head + statistics kernel (one pass over W).
+// Fused RMSNorm + LM head + statistics, one pass over W for rows [row0, row0 + rows).
 struct StatsArgs {
   const void* W;          // [V][d]
   const void* gamma;      // [d]
@@ -111,17 +107,35 @@ struct StatsArgs {
   float eps;
   float* logits;          // [M][V]
   const float* G;         // [B][K][V] draft logits, or null
-  const int* drafts;      // [B][K], or null
   int B, K;               // block structure (K = -1: plain rows, no statistics)
   float T, c;             // temperature and log2(e) / T
   int stats;              // write per-row partial statistics
   int want_q;             // also draft-logit statistics (softmax proposal, T > 0)
   RowStat* partial;       // [gridDim][M]
-  double* zd;             // [M] exact logit at the row's draft token (draft rows)
-  int finalize;           // FinalizeKind, only on the last pass
-  uint32_t* counter;
+  float* rnorm;           // [M] RMSNorm factor of every row (written by workgroup 0), or null
+};
+
+enum FinalizeKind { kFinalizeVerify = 1, kFinalizeScore = 2 };
+
+// Combine the partials of a request, then the acceptance scan (verify) or the outcome
+// marginals (score).  One workgroup per request.
+struct FinalArgs {
+  const void* W;
+  const void* gamma;
+  const void* hidden;
+  int64_t V;
+  int d;
+  int dtype;
+  const float* G;
+  const int* drafts;
+  int B, K;
+  float T;
   int mode;
+  int kind;               // FinalizeKind
   uint64_t seed, offset;
+  int P;                  // partial records per row
+  const RowStat* partial;
+  const float* rnorm;
   int* n_accepted;
   int* committed;
   uint32_t* flags;        // may be null
@@ -145,9 +159,8 @@ struct SampleArgs {
   const RowFinal* rowfinal;
   const ReqState* req;
   double* zs;             // [B][slices][2]
-  uint32_t* counter;      // [B]
   int* committed;
-  uint32_t* flags;
+  uint32_t* flags;        // may be null
 };
 
 struct ScoreArgs {
@@ -163,18 +176,17 @@ struct ScoreArgs {
   const ReqState* req;
   double* zs;             // [B][K+1][slices]
   Cand* cand;             // [B][K+1][slices][top_n+1]
-  uint32_t* counter;      // [B]
   int* out_len;
   int* out_token;
   float* out_prob;
-  uint32_t* flags;
+  uint32_t* flags;        // may be null
 };
 
 // Host-side launchers (jsv_kernels.hip).  Return hipSuccess or the launch error.
 // `nks` is hidden / (kWaves * elements per k-step); the launcher picks the instance.
 bool stats_supported(int dtype, int nks);
-hipError_t launch_stats(int dtype, int nks, int rows, int grid, const StatsArgs& a,
-                        hipStream_t stream);
+hipError_t launch_stats(int dtype, int nks, int grid, const StatsArgs& a, hipStream_t stream);
+hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
 

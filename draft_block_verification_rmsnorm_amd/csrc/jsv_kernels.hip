@@ -1,21 +1,21 @@
 // HIP kernels of libjsverify for gfx950 (MI355X).
 //
-//   stats_kernel   fused final RMSNorm + LM head (bf16 MFMA 16x16x32, or f32 MFMA 16x16x4)
-//                  with an epilogue that writes the logits and per-row online softmax
-//                  statistics; the last workgroup to finish combines the statistics and
-//                  runs the acceptance scan (JetSpec++ paper §3, App. F.3) or the outcome
-//                  marginals (§4.2 Eq. 6).
-//   sample_kernel  bonus token of each request by inverse CDF over the residual of the
-//                  rejected row (§3), spread over vocabulary slices; the last slice to
-//                  finish locates the CDF step.
-//   score_kernel   per (request, row, slice) residual mass and top-(N+1) candidates; the
-//                  last workgroup of a request merges them into the top-N outcomes (§4.2
-//                  Eq. 7, App. B.1).
+//   stats_kernel     fused final RMSNorm + LM head (bf16 MFMA 16x16x32, or f32 MFMA
+//                    16x16x4) whose epilogue writes the logits and per-row online softmax
+//                    statistics of its vocabulary range (JetSpec++ paper §4.2 "Decoder").
+//   finalize_kernel  per request: combine the statistics, the exact logit at each draft
+//                    token, then the acceptance scan (paper §3, App. F.3) or the outcome
+//                    marginals (§4.2 Eq. 6).
+//   slice_sum_kernel / locate_kernel
+//                    bonus token by inverse CDF over the residual of the rejected row
+//                    (§3): residual mass per vocabulary slice, then the CDF step.
+//   score_slice_kernel / score_merge_kernel
+//                    residual mass and top-(N+1) columns per (row, slice), then the top-N
+//                    outcomes of the request (§4.2 Eq. 7, App. B.1).
+// Kernels hand results to each other only through kernel boundaries on one stream.
 #include <float.h>
 #include <limits.h>
 #include <math.h>
-
-#include <type_traits>
 
 #include "jsv_internal.h"
 #include "jsverify.h"
@@ -23,14 +23,18 @@
 namespace jsv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr double kAcceptTie = 1e-4;
 constexpr float kLogitGapTie = 1e-3f;
 constexpr double kCdfTie = 1e-8;
 constexpr double kTopNTie = 1e-3;
 constexpr double kLog2eD = 1.4426950408889634074;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every resource used here
+constexpr int kRsrcWord3 = 0x00020000;         // raw 32-bit-element buffer, gfx9 family
 
 // ------------------------------------------------------------------------------------
 // Philox4x32-10, from the SC'11 paper by Salmon, Moraes, Dror and Shaw.
@@ -55,6 +59,25 @@ __device__ inline void row_uniforms(uint64_t seed, uint64_t offset, int b, int i
   philox4x32_10(c, uint32_t(seed), uint32_t(seed >> 32));
   u = double(c[0]) * 0x1p-32;
   v = double((uint64_t(c[1]) << 21) | uint64_t(c[2] >> 11)) * 0x1p-53;
+}
+
+// ------------------------------------------------------------------------------------
+// Memory helpers.  Buffer accesses past num_records return zero (loads) or are dropped
+// (stores), so the streaming loops need no branches around their memory operations.
+__device__ inline rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : uint32_t(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+__device__ inline uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// The 32-bit buffer builtins move integer words: floats cross them as bit patterns.
+__device__ inline float bload4f(rsrc_t r, uint32_t voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+}
+__device__ inline void bstore4f(float x, rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, 0, 0);
 }
 
 // ------------------------------------------------------------------------------------
@@ -87,6 +110,25 @@ __device__ inline void unpack(const uint4& q, float* x) {
   }
 }
 
+// Sum of squares of one 16-byte group, in float64 (exact for bf16 inputs).
+template <int DT>
+__device__ inline double sumsq16(const uint4& q) {
+  constexpr int EPL = Elem<DT>::EPL;
+  float x[EPL];
+  unpack<DT>(q, x);
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s = fma(double(x[e]), double(x[e]), s);
+  return s;
+}
+
+// RMSNorm factor r = fp32(1 / sqrt(mean(h^2) + eps)) from the float64 sum of squares:
+// r decides the rounding of every normalised element, so it is taken at a precision
+// where a different summation order cannot move it.
+__device__ inline float rms_factor(double ss, int d, float eps) {
+  return float(1.0 / sqrt(ss / double(d) + double(eps)));
+}
+
 // x = round_dtype( fp32( fp32(h * r) * gamma ) ) for one 16-byte group of elements.
 template <int DT>
 __device__ inline uint4 norm_pack(const uint4& hq, const uint4& gq, float r) {
@@ -111,9 +153,9 @@ __device__ inline uint4 norm_pack(const uint4& hq, const uint4& gq, float r) {
   }
 }
 
-// acc += A(16x(k-step)) * B((k-step)x16).  Lane l holds row l%16 of A and column l%16 of
-// B over the same k positions (lane group l/16 owns k = 8*(l/16)..+7 for bf16, 4 elements
-// consumed by four 16x16x4 steps for f32), so any hardware k order gives the same sum.
+// acc += A(16 x k-step) * B(k-step x 16).  Lane l holds row l%16 of A and column l%16 of
+// B over the same k positions (lane group l/16 owns its 16 bytes of the k-step; for f32
+// the four elements feed four 16x16x4 steps), so any hardware k order gives the same sum.
 template <int DT>
 __device__ inline floatx4 mfma_step(const uint4& a, const uint4& b, floatx4 acc) {
   if constexpr (DT == JSV_BF16) {
@@ -124,6 +166,26 @@ __device__ inline floatx4 mfma_step(const uint4& a, const uint4& b, floatx4 acc)
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+    return acc;
+  }
+}
+
+// x += W(16 B of one row) . xhat(16 B of one hidden row) on the VALU.
+template <int DT>
+__device__ inline float dot16(const uint4& wq, const uint4& xq, float acc) {
+  if constexpr (DT == JSV_BF16) {
+    const uint32_t a[4] = {wq.x, wq.y, wq.z, wq.w};
+    const uint32_t b[4] = {xq.x, xq.y, xq.z, xq.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[e]),
+                                            __builtin_bit_cast(bf16x2, b[e]), acc, false);
+    return acc;
+  } else {
+    acc = fmaf(__uint_as_float(wq.x), __uint_as_float(xq.x), acc);
+    acc = fmaf(__uint_as_float(wq.y), __uint_as_float(xq.y), acc);
+    acc = fmaf(__uint_as_float(wq.z), __uint_as_float(xq.z), acc);
+    acc = fmaf(__uint_as_float(wq.w), __uint_as_float(xq.w), acc);
     return acc;
   }
 }
@@ -180,164 +242,13 @@ __device__ inline Stat stat_load(const RowStat& r) {
   return s;
 }
 
-// ------------------------------------------------------------------------------------
-// Last-workgroup finalize of the LM-head kernel: combine every workgroup's partial
-// statistics, then per request run the acceptance scan (verify) or the outcome
-// marginals (score).  Runs in one workgroup of kThreads threads.
-__device__ void finalize_block(const StatsArgs& a, int P, Stat* rows_sh) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const bool soft = a.T > 0.f;
-  const float c = a.c;
-  const int M = a.M;
-  // Phase A: row r is combined by wave r % kWaves; lanes stride over the partials.
-  for (int r0 = w; r0 < M; r0 += 2 * kWaves) {
-    Stat acc[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) stat_init(acc[u]);
-#pragma unroll 4
-    for (int p = lane; p < P; p += kWave) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = r0 + u * kWaves;
-        if (r < M) stat_merge(acc[u], stat_load(a.partial[(size_t)p * M + r]), c, soft);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      for (int off = 32; off > 0; off >>= 1) stat_merge(acc[u], stat_shfl_xor(acc[u], off), c, soft);
-      const int r = r0 + u * kWaves;
-      if (lane == 0 && r < M) rows_sh[r] = acc[u];
-    }
-  }
-  __syncthreads();
-  if (a.K < 0) return;
-
-  // Phase B: wave b handles request b; lane i handles row i.
-  const int K = a.K, R = K + 1;
-  const int64_t V = a.V;
-  const double cd = double(kLog2eD) / double(a.T);
-  for (int b = w; b < a.B; b += kWaves) {
-    const bool act = lane <= K;
-    const int row = b * R + lane;
-    Stat st;
-    stat_init(st);
-    if (act) st = rows_sh[row];
-    const int di = (lane < K) ? a.drafts[b * K + lane] : -1;
-    const bool bad = act && ((st.flags & JSV_FLAG_INVALID) || (lane < K && (di < 0 || (int64_t)di >= V)));
-    const bool invalid = __ballot(bad) != 0;
-    if (invalid) {
-      if (act && a.finalize == kFinalizeVerify) a.committed[row] = -1;
-      if (lane == 0) {
-        if (a.finalize == kFinalizeVerify) a.n_accepted[b] = -1;
-        if (a.flags) a.flags[b] = JSV_FLAG_INVALID;
-        ReqState rq{}; rq.k = -1; rq.flags = JSV_FLAG_INVALID; a.req[b] = rq;
-      }
-      if (a.finalize == kFinalizeScore) {
-        if (lane < a.top_n) {
-          a.out_len[b * a.top_n + lane] = -1;
-          a.out_token[b * a.top_n + lane] = -1;
-          a.out_prob[b * a.top_n + lane] = 0.f;
-        }
-        if (act && a.len_marginal) a.len_marginal[row] = 0.0;
-      }
-      continue;
-    }
-
-    double alpha = 0.0;
-    if (!soft) {
-      // Greedy verification: accept while the draft equals the row's argmax.
-      alpha = (lane < K && di == st.idx) ? 1.0 : 0.0;
-    } else if (lane < K) {
-      // p(d) from the float64 logit at the draft token (computed in the prologue), so
-      // that alpha and 1 - alpha keep their digits when alpha is close to 1.
-      const double zd = a.zd[row];
-      const double pd = exp2((zd - double(st.m)) * cd) / st.s;
-      if (a.mode == JSV_PROPOSAL_POINT) {
-        alpha = pd;
-      } else {
-        const double gd = a.G[(size_t)(b * K + lane) * V + di];
-        const double qd = exp2((gd - double(st.mq)) * cd) / st.sq;
-        alpha = (pd == 0.0) ? 0.0 : (pd >= qd ? 1.0 : pd / qd);
-      }
-    }
-
-    uint32_t f = 0;
-    int k = K;
-    double vk = 0.0;
-    if (!soft) {
-      const uint64_t rej = __ballot(lane < K && alpha == 0.0);
-      k = rej ? __builtin_ctzll(rej) : K;
-      const bool gap = act && lane <= k && (st.m - st.top2) < kLogitGapTie;
-      if (__ballot(gap)) f |= JSV_FLAG_LOGIT_GAP;
-    } else if (a.finalize == kFinalizeVerify) {
-      double u = 0.0, v = 0.0;
-      if (act) row_uniforms(a.seed, a.offset, b, lane, u, v);
-      const uint64_t rej = __ballot(lane < K && !(u < alpha));
-      k = rej ? __builtin_ctzll(rej) : K;
-      const bool tie = lane < K && lane <= k && fabs(u - alpha) < kAcceptTie;
-      if (__ballot(tie)) f |= JSV_FLAG_ACCEPT_TIE;
-      vk = __shfl(v, k);
-    }
-    const int bonus = __shfl(st.idx, k);
-
-    // A_i = prod_{j<i} alpha_j (probability of reaching row i).
-    double A = 1.0;
-    for (int j = 0; j < K; ++j) {
-      const double aj = __shfl(alpha, j);
-      if (j < lane) A *= aj;
-    }
-
-    if (act) {
-      RowFinal rf{};
-      rf.s = st.s; rf.sq = st.sq; rf.alpha = alpha; rf.A = A;
-      rf.m = st.m; rf.top2 = st.top2; rf.mq = st.mq; rf.idx = st.idx; rf.flags = st.flags;
-      a.rowfinal[row] = rf;
-    }
-    if (a.finalize == kFinalizeVerify) {
-      if (act) a.committed[row] = (lane < k) ? di : ((lane == k && !soft) ? bonus : -1);
-      if (lane == 0) {
-        a.n_accepted[b] = k;
-        if (a.flags) a.flags[b] = f;
-        ReqState rq{}; rq.vk = vk; rq.k = k; rq.flags = f; a.req[b] = rq;
-      }
-    } else {  // score
-      if (act && a.len_marginal) {
-        a.len_marginal[row] = soft ? ((lane < K) ? A * (1.0 - alpha) : A) : (lane == k ? 1.0 : 0.0);
-      }
-      if (!soft) {  // all mass on the greedy outcome
-        if (lane < a.top_n) {
-          a.out_len[b * a.top_n + lane] = (lane == 0) ? k : -1;
-          a.out_token[b * a.top_n + lane] = (lane == 0) ? bonus : -1;
-          a.out_prob[b * a.top_n + lane] = (lane == 0) ? 1.f : 0.f;
-        }
-      }
-      if (lane == 0) {
-        if (a.flags) a.flags[b] = f;
-        ReqState rq{}; rq.k = k; rq.flags = f; a.req[b] = rq;
-      }
-    }
-  }
-}
-
-// x += W(16 B of one row) . xhat(16 B of one hidden row) on the VALU (rows beyond the
-// MFMA tiles).
-template <int DT>
-__device__ inline float dot16(const uint4& wq, const uint4& xq, float acc) {
-  if constexpr (DT == JSV_BF16) {
-    const uint32_t a[4] = {wq.x, wq.y, wq.z, wq.w};
-    const uint32_t b[4] = {xq.x, xq.y, xq.z, xq.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[e]),
-                                            __builtin_bit_cast(bf16x2, b[e]), acc, false);
-    return acc;
-  } else {
-    acc = fmaf(__uint_as_float(wq.x), __uint_as_float(xq.x), acc);
-    acc = fmaf(__uint_as_float(wq.y), __uint_as_float(xq.y), acc);
-    acc = fmaf(__uint_as_float(wq.z), __uint_as_float(xq.z), acc);
-    acc = fmaf(__uint_as_float(wq.w), __uint_as_float(xq.w), acc);
-    return acc;
-  }
+// Fold one value into (max, sum exp) without branches; ze = -inf contributes nothing.
+__device__ inline void fold(float& m, double& s, float ze, float c) {
+  const float nm = fmaxf(m, ze);
+  const double sc = nm == -INFINITY ? 0.0 : double(exp2f((m - nm) * c));
+  const double ad = nm == -INFINITY ? 0.0 : double(exp2f((ze - nm) * c));
+  s = s * sc + ad;
+  m = nm;
 }
 
 // Prefetch window: the largest divisor of NKS whose W registers fit beside the
@@ -353,25 +264,26 @@ constexpr int pick_window(int NT, int NKS) {
 // [g0, g1); its 8 waves split d into equal k-slices.  Each wave keeps the normalised
 // hidden states of its slice for the NT full 16-token tiles in registers (MFMA B
 // operand) and streams the same slice of W straight into MFMA A operands, D k-steps
-// ahead; NX further rows (at most one) are dotted on the VALU against a copy of their
+// ahead, through a buffer resource over the workgroup's rows (rows past the vocabulary
+// read as zero).  NX further rows (at most one) are dotted on the VALU against their
 // normalised state in LDS.  Per group the 8 partial tiles are summed through LDS (in
 // fp64, fixed order) and thread (token jj, column ii) folds its logit into running
-// statistics.  The logit at each row's draft token is recomputed exactly (fp64) in the
-// prologue for the acceptance test.
+// statistics; at the end the 16 threads of a token merge theirs into one partial.
 template <int DT, int NT, int NX, int NKS>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   constexpr int EPL = Elem<DT>::EPL, ESZ = Elem<DT>::ESZ, KS = 4 * EPL;
   constexpr int D = pick_window(NT, NKS);
   constexpr int NTOK = NT * 16 + NX;
-  constexpr int NEP = (NTOK + 31) / 32;   // tokens per epilogue thread
-  constexpr int XLEN = kWaves * NKS * 4;  // 16-byte groups per hidden row
+  constexpr int NEP = (NTOK + 31) / 32;     // tokens per epilogue thread
+  constexpr int XLEN = kWaves * NKS * 4;    // 16-byte groups per hidden row
+  constexpr int XPT = (XLEN + kThreads - 1) / kThreads;
   constexpr int NT1 = NT > 0 ? NT : 1, NX1 = NX > 0 ? NX : 1;
   static_assert(NTOK >= 1 && NTOK <= kRowsPerPass && NX <= 1, "tiling");
   __shared__ floatx4 red[2][kWaves][NT1][kWave];
   __shared__ float redx[2][kWaves][NX1][16];
   __shared__ uint4 xrow[NX1][XLEN];
+  __shared__ double ssq[kWaves][kRowsPerPass];
   __shared__ float rnorm[kRowsPerPass];
-  __shared__ uint32_t last_flag;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int P = gridDim.x, wg = blockIdx.x;
@@ -380,134 +292,140 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   const int64_t ngroups = (V + 15) >> 4;
   const int64_t g0 = ngroups * wg / P, g1 = ngroups * (wg + 1) / P;
   const int kb = w * (NKS * KS) + (lane >> 4) * EPL;
-  const char* Wb = static_cast<const char*>(a.W);
-  const int vr = lane & 15;
+  const uint32_t rowbytes = uint32_t(d) * ESZ;
 
-  // Rows past the vocabulary re-read row V-1: the loads stay branch-free (so the
-  // compiler can keep the whole window in flight) and those output rows are never used.
+  // W rows [16*g0, min(V, 16*g1)) as one buffer; group g of it at soffset (g-g0)*16 rows.
+  const int64_t wrow0 = g0 * 16;
+  const int64_t wrows = (V < g1 * 16 ? V : g1 * 16) - wrow0;
+  const rsrc_t wr = make_rsrc(static_cast<const char*>(a.W) + (size_t)wrow0 * rowbytes,
+                              (uint64_t)(wrows > 0 ? wrows : 0) * rowbytes);
+  const uint32_t wvoff = uint32_t(lane & 15) * rowbytes + uint32_t(kb) * ESZ;
   auto wload = [&](int64_t g, int s) -> uint4 {
-    int64_t v = g * 16 + vr;
-    v = v < V ? v : V - 1;
-    return *reinterpret_cast<const uint4*>(Wb + ((size_t)v * d + kb + s * KS) * ESZ);
+    return bload16(wr, wvoff + uint32_t(s * KS * ESZ), uint32_t(g - g0) * 16u * rowbytes);
   };
 
   // Start streaming W before the norm prologue.
   uint4 fr[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) fr[j] = wload(g0 < g1 ? g0 : 0, j);
+  for (int j = 0; j < D; ++j) fr[j] = wload(g0, j);
 
-  // RMSNorm factors r = 1 / sqrt(mean(h^2) + eps) of the rows of this pass, in float64
-  // and rounded once to float32: r decides the rounding of every normalised element,
-  // so it is taken at a precision where a different summation order cannot move it.
-  const char* Hb = static_cast<const char*>(a.hidden);
+  // ---- RMSNorm of the rows of this pass ----------------------------------------------
+  const char* Hb = static_cast<const char*>(a.hidden) + (size_t)a.row0 * rowbytes;
   const char* Gm = static_cast<const char*>(a.gamma);
-  for (int r = w; r < a.rows; r += kWaves) {
-    const char* hr = Hb + (size_t)(a.row0 + r) * d * ESZ;
-    double ss = 0.0;
-    for (int k = lane * EPL; k < d; k += kWave * EPL) {
-      float x[EPL];
-      unpack<DT>(*reinterpret_cast<const uint4*>(hr + (size_t)k * ESZ), x);
+  const rsrc_t hr = make_rsrc(Hb, (uint64_t)a.rows * rowbytes);
+  const rsrc_t gr = make_rsrc(Gm, rowbytes);
+  uint32_t tokoff[NT1];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ss = fma(double(x[e]), double(x[e]), ss);
+  for (int t = 0; t < NT1; ++t) {
+    const int tok = t * 16 + (lane & 15);
+    tokoff[t] = (t < NT && tok < a.rows) ? uint32_t(tok) * rowbytes : kOutOfRange;
+  }
+  // Sums of squares of this wave's slice of every tile token (padding tokens read zeros).
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    double ps = 0.0;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      ps += sumsq16<DT>(bload16(hr, tokoff[t] + uint32_t(kb + s * KS) * ESZ, 0));
+      if ((s & 3) == 3) asm volatile("" ::: "memory");  // bound the loads in flight here
     }
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if (lane == 0) rnorm[r] = float(1.0 / sqrt(ss / double(d) + double(a.eps)));
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    if (lane < 16) ssq[w][t * 16 + lane] = ps;
+  }
+  // The VALU row: block-wide, XPT 16-byte groups per thread.
+  uint4 xh[NX1][XPT];
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    double ps = 0.0;
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int q = tid + j * kThreads;
+      const uint32_t off = (q < XLEN) ? uint32_t(NT * 16 + x) * rowbytes + uint32_t(q) * 16u : kOutOfRange;
+      xh[x][j] = bload16(hr, off, 0);
+      ps += sumsq16<DT>(xh[x][j]);
+    }
+    for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+    if (lane == 0) ssq[w][NT * 16 + x] = ps;
+  }
+  __syncthreads();
+  if (tid < a.rows) {
+    double ss = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) ss += ssq[w2][tid];  // fixed order over waves
+    const float r = rms_factor(ss, d, a.eps);
+    rnorm[tid] = r;
+    if (wg == 0 && a.rnorm != nullptr) a.rnorm[a.row0 + tid] = r;
   }
   __syncthreads();
 
-  // Exact (fp64) logit at the draft token of each draft row of this pass: row r is done
-  // by wave (r / P) % 8 of workgroup r % P, overlapping the W stream.
-  if (a.stats && a.K >= 0) {
-    for (int r = wg + P * w; r < a.rows; r += P * kWaves) {
-      const int row = a.row0 + r;
-      const int b = row / (a.K + 1), i = row - b * (a.K + 1);
-      if (i >= a.K) continue;
-      const int dt = a.drafts[b * a.K + i];
-      if (dt < 0 || (int64_t)dt >= V) continue;
-      const char* hr = Hb + (size_t)row * d * ESZ;
-      const char* wr = Wb + (size_t)dt * d * ESZ;
-      double acc = 0.0;
-      for (int k = lane * EPL; k < d; k += kWave * EPL) {
-        const uint4 xq = norm_pack<DT>(*reinterpret_cast<const uint4*>(hr + (size_t)k * ESZ),
-                                       *reinterpret_cast<const uint4*>(Gm + (size_t)k * ESZ), rnorm[r]);
-        float xv[EPL], wv[EPL];
-        unpack<DT>(xq, xv);
-        unpack<DT>(*reinterpret_cast<const uint4*>(wr + (size_t)k * ESZ), wv);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc += double(xv[e]) * double(wv[e]);
-      }
-      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-      if (lane == 0) a.zd[row] = acc;
-    }
-  }
-
-  // Normalised hidden states of this wave's k-slice for the MFMA tiles.  Padding
-  // tokens read row 0 of the pass with r = 0 (their output columns are never used).
+  // Normalised hidden states of this wave's k-slice for the MFMA tiles (padding tokens
+  // get r = 0; their output columns are never used).  The rows are re-read (they are
+  // in cache by now) rather than held in registers across the reduction.
   uint4 xf[NT1][NKS];
   {
     float rt[NT1];
-    const char* hrt[NT1];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int tok = t * 16 + (lane & 15);
-      const bool ok = tok < a.rows;
-      rt[t] = ok ? rnorm[tok] : 0.f;
-      hrt[t] = Hb + (size_t)(a.row0 + (ok ? tok : 0)) * d * ESZ;
+      rt[t] = tok < a.rows ? rnorm[tok] : 0.f;
     }
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const int k = kb + s * KS;
-      const uint4 gq = *reinterpret_cast<const uint4*>(Gm + (size_t)k * ESZ);
+      const uint4 g = bload16(gr, uint32_t(kb + s * KS) * ESZ, 0);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        xf[t][s] = norm_pack<DT>(*reinterpret_cast<const uint4*>(hrt[t] + (size_t)k * ESZ), gq, rt[t]);
-      // keep at most four k-steps of loads in flight here (register pressure)
-      if ((s & 3) == 3) asm volatile("" ::: "memory");
+        xf[t][s] = norm_pack<DT>(bload16(hr, tokoff[t] + uint32_t(kb + s * KS) * ESZ, 0), g, rt[t]);
+      if ((s & 3) == 3) asm volatile("" ::: "memory");  // bound the loads in flight here
     }
   }
-  // Rows beyond the tiles: whole normalised row in LDS.
+  // The VALU row in LDS.
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
-    const int tok = NT * 16 + x;
-    const char* hr = Hb + (size_t)(a.row0 + tok) * d * ESZ;
-    const float r = rnorm[tok];
-    for (int q = tid; q < XLEN; q += kThreads)
-      xrow[x][q] = norm_pack<DT>(*reinterpret_cast<const uint4*>(hr + (size_t)q * 16),
-                                 *reinterpret_cast<const uint4*>(Gm + (size_t)q * 16), r);
+    const float r = rnorm[NT * 16 + x];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int q = tid + j * kThreads;
+      if (q < XLEN) xrow[x][q] = norm_pack<DT>(xh[x][j], bload16(gr, uint32_t(q) * 16u, 0), r);
+    }
   }
   if (NX > 0) __syncthreads();
 
-  // Epilogue identity: tokens jj = tid/16 (+32), vocabulary column ii of the group.
+  // ---- epilogue identity: tokens jj = tid/16 (+32), vocabulary column ii ---------------
   const int ii = tid & 15;
   const bool soft = a.T > 0.f;
   const float c = a.c;
-  int jj[NEP], row[NEP];
-  bool tok_ok[NEP];
-  const float* gsrc[NEP];
+  // Logits rows of this pass, and the draft-logit rows of the requests it touches.
+  const rsrc_t lr = make_rsrc(a.logits + (size_t)a.row0 * V, (uint64_t)a.rows * (uint64_t)V * 4u);
+  const int qrow0 = a.want_q ? (a.row0 / (a.K + 1)) * a.K : 0;
+  const int qrows = a.want_q ? ((a.row0 + a.rows - 1) / (a.K + 1)) * a.K + a.K - qrow0 : 0;
+  const rsrc_t qr = make_rsrc(a.G + (size_t)qrow0 * V, (uint64_t)qrows * (uint64_t)V * 4u);
+  int jj[NEP];
+  bool tok_ok[NEP], qrow[NEP];
+  uint32_t loff[NEP], qoff[NEP];
   Stat st[NEP];
 #pragma unroll
   for (int e = 0; e < NEP; ++e) {
     jj[e] = (tid >> 4) + 32 * e;
     tok_ok[e] = jj[e] < NTOK && jj[e] < a.rows;
-    row[e] = a.row0 + (tok_ok[e] ? jj[e] : 0);
-    gsrc[e] = nullptr;
+    const int row = a.row0 + (tok_ok[e] ? jj[e] : 0);
+    loff[e] = uint32_t(row - a.row0) * uint32_t(V) * 4u;
+    qrow[e] = false;
+    qoff[e] = kOutOfRange;
     if (a.want_q && tok_ok[e]) {
-      const int b = row[e] / (a.K + 1), i = row[e] - b * (a.K + 1);
-      if (i < a.K) gsrc[e] = a.G + (size_t)(b * a.K + i) * V;
+      const int b = row / (a.K + 1), i = row - b * (a.K + 1);
+      if (i < a.K) { qrow[e] = true; qoff[e] = uint32_t(b * a.K + i - qrow0) * uint32_t(V) * 4u; }
     }
     stat_init(st[e]);
   }
 
   int buf = 0;
-  // One group: MFMAs over this wave's k-slice, refilling the window from the next group
-  // (REFILL) or only from this one (the last group), then the LDS reduction + epilogue.
-  auto group = [&](int64_t g, auto refill_tag) {
-    constexpr bool REFILL = decltype(refill_tag)::value;
+  for (int64_t g = g0; g < g1; ++g) {
     const int64_t v = g * 16 + ii;
-    const int64_t vc = v < V ? v : V - 1;
+    const bool vok = v < V;
     float gv[NEP];
 #pragma unroll
-    for (int e = 0; e < NEP; ++e) gv[e] = gsrc[e] ? gsrc[e][vc] : 0.f;
+    for (int e = 0; e < NEP; ++e) gv[e] = bload4f(qr, qoff[e] + uint32_t(v) * 4u);
     floatx4 acc[NT1];
     float xacc[NX1];
 #pragma unroll
@@ -521,10 +439,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       for (int t = 0; t < NT; ++t) acc[t] = mfma_step<DT>(f, xf[t][s], acc[t]);
 #pragma unroll
       for (int x = 0; x < NX; ++x) xacc[x] = dot16<DT>(f, xrow[x][(kb + s * KS) / EPL], xacc[x]);
+      // refill this slot D steps ahead (past the last group the loads read zeros)
       const bool nxt = (s + D) >= NKS;
-      const int sn = nxt ? (s + D - NKS) : (s + D);
-      if (!nxt) fr[s % D] = wload(g, sn);
-      else if (REFILL) fr[s % D] = wload(g + 1, sn);
+      fr[s % D] = wload(nxt ? g + 1 : g, nxt ? (s + D - NKS) : (s + D));
     }
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
@@ -550,38 +467,24 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
         for (int w2 = 0; w2 < kWaves; ++w2) zz += double(redx[buf][w2][x][ii]);
       }
       const float z = float(zz);
-      if (tok_ok[e] && v < V) {
-        a.logits[(size_t)row[e] * V + v] = z;
-        if (a.stats) {
-          Stat& S = st[e];
-          if (!(fabsf(z) <= FLT_MAX)) {
-            S.flags |= JSV_FLAG_INVALID;
-          } else if (z > S.m) {
-            if (soft) S.s = S.s * double(exp2f((S.m - z) * c)) + 1.0;
-            S.top2 = S.m; S.m = z; S.idx = int(v);
-          } else {
-            S.top2 = fmaxf(S.top2, z);
-            if (soft) S.s += double(exp2f((z - S.m) * c));
-          }
-          if (gsrc[e] != nullptr) {
-            const float q = gv[e];
-            if (!(fabsf(q) <= FLT_MAX)) {
-              S.flags |= JSV_FLAG_INVALID;
-            } else if (q > S.mq) {
-              S.sq = S.sq * double(exp2f((S.mq - q) * c)) + 1.0;
-              S.mq = q;
-            } else {
-              S.sq += double(exp2f((q - S.mq) * c));
-            }
-          }
+      const bool valid = tok_ok[e] && vok;
+      bstore4f(z, lr, valid ? loff[e] + uint32_t(v) * 4u : kOutOfRange);
+      if (a.stats) {
+        Stat& S = st[e];
+        const bool fin = fabsf(z) <= FLT_MAX;
+        if (valid && !fin) S.flags |= JSV_FLAG_INVALID;
+        const float ze = (valid && fin) ? z : -INFINITY;
+        if (ze > S.m) { S.top2 = S.m; S.idx = int(v); } else { S.top2 = fmaxf(S.top2, ze); }
+        if (soft) fold(S.m, S.s, ze, c); else S.m = fmaxf(S.m, ze);
+        if (qrow[e]) {
+          const float q = gv[e];
+          const bool qf = fabsf(q) <= FLT_MAX;
+          if (vok && !qf) S.flags |= JSV_FLAG_INVALID;
+          fold(S.mq, S.sq, (vok && qf) ? q : -INFINITY, c);
         }
       }
     }
     buf ^= 1;
-  };
-  if (g0 < g1) {
-    for (int64_t g = g0; g + 1 < g1; ++g) group(g, std::true_type{});
-    group(g1 - 1, std::false_type{});
   }
 
   if (!a.stats) return;
@@ -592,21 +495,190 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       RowStat rs{};
       rs.s = st[e].s; rs.sq = st[e].sq; rs.m = st[e].m; rs.top2 = st[e].top2; rs.mq = st[e].mq;
       rs.idx = st[e].idx; rs.flags = st[e].flags;
-      a.partial[(size_t)wg * a.M + row[e]] = rs;
+      a.partial[(size_t)wg * a.M + a.row0 + jj[e]] = rs;
     }
   }
-  if (a.finalize == kFinalizeNone) return;
+}
 
-  // Last workgroup to arrive finalizes (no waiting: the others simply exit).
-  __threadfence();
+// ------------------------------------------------------------------------------------
+// Per-request finalize: grid B, kThreads threads.
+//   phase 0  exact (fp64) logit at each draft token, from the normalised row and W[d]
+//            (T > 0: alpha and 1 - alpha keep their digits when alpha is close to 1);
+//   phase A  combine every LM-head workgroup's partial statistics of the K+1 rows;
+//   phase B  wave 0, lane i = row i: acceptance probabilities, the scan to the first
+//            rejection with the Philox uniforms (verify) or the outcome marginals (score).
+template <int DT>
+__device__ void exact_draft_logits(const FinalArgs& a, int b, double* zd_sh) {
+  constexpr int EPL = Elem<DT>::EPL, ESZ = Elem<DT>::ESZ;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int K = a.K, R = K + 1, d = a.d;
+  for (int i = w; i < K; i += kWaves) {
+    const int dt = a.drafts[b * K + i];
+    if (dt < 0 || (int64_t)dt >= a.V) continue;
+    const int row = b * R + i;
+    const float r = a.rnorm[row];
+    const char* hrow = static_cast<const char*>(a.hidden) + (size_t)row * d * ESZ;
+    const char* wrow = static_cast<const char*>(a.W) + (size_t)dt * d * ESZ;
+    const char* gm = static_cast<const char*>(a.gamma);
+    double acc = 0.0;
+    for (int k = lane * EPL; k < d; k += kWave * EPL) {
+      const uint4 xq = norm_pack<DT>(*reinterpret_cast<const uint4*>(hrow + (size_t)k * ESZ),
+                                     *reinterpret_cast<const uint4*>(gm + (size_t)k * ESZ), r);
+      float xv[EPL], wv[EPL];
+      unpack<DT>(xq, xv);
+      unpack<DT>(*reinterpret_cast<const uint4*>(wrow + (size_t)k * ESZ), wv);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc += double(xv[e]) * double(wv[e]);
+    }
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) zd_sh[i] = acc;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int K = a.K, R = K + 1, P = a.P;
+  const int64_t V = a.V;
+  const bool soft = a.T > 0.f;
+  const float c = soft ? float(kLog2eD / double(a.T)) : 0.f;
+  const double cd = soft ? kLog2eD / double(a.T) : 0.0;
+  __shared__ Stat rows_sh[kMaxK + 1];
+  __shared__ double zd_sh[kMaxK];
+
+  if (soft) {
+    if (a.dtype == JSV_BF16) exact_draft_logits<JSV_BF16>(a, b, zd_sh);
+    else exact_draft_logits<JSV_F32>(a, b, zd_sh);
+  }
+  // Phase A: row i by wave i % kWaves, two rows per pass with their loads in flight.
+  const int M = a.B * R;
+  for (int i0 = w; i0 < R; i0 += 2 * kWaves) {
+    Stat acc[2];
+    stat_init(acc[0]);
+    stat_init(acc[1]);
+    for (int p0 = 0; p0 < P; p0 += 4 * kWave) {
+      RowStat ld[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + u * kWaves, p = p0 + j * kWave + lane;
+          if (i < R && p < P) {
+            ld[u][j] = a.partial[(size_t)p * M + b * R + i];
+          } else {
+            ld[u][j] = RowStat{};
+            ld[u][j].m = -INFINITY; ld[u][j].top2 = -INFINITY; ld[u][j].mq = -INFINITY;
+            ld[u][j].idx = INT_MAX;
+          }
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) stat_merge(acc[u], stat_load(ld[u][j]), c, soft);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      for (int off = 32; off > 0; off >>= 1) stat_merge(acc[u], stat_shfl_xor(acc[u], off), c, soft);
+      const int i = i0 + u * kWaves;
+      if (lane == 0 && i < R) rows_sh[i] = acc[u];
+    }
+  }
   __syncthreads();
-  if (tid == 0) last_flag = (atomicAdd(a.counter, 1u) == uint32_t(P - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  __shared__ Stat rows_sh[kMaxB * (kMaxK + 1)];
-  finalize_block(a, P, rows_sh);
-  if (tid == 0) *a.counter = 0u;
+  if (w != 0) return;
+
+  // Phase B: lane i handles row i of request b.
+  const bool act = lane <= K;
+  const int row = b * R + lane;
+  Stat st;
+  stat_init(st);
+  if (act) st = rows_sh[lane];
+  const int di = (lane < K) ? a.drafts[b * K + lane] : -1;
+  const bool bad = act && ((st.flags & JSV_FLAG_INVALID) || (lane < K && (di < 0 || (int64_t)di >= V)));
+  if (__ballot(bad) != 0) {
+    if (act && a.kind == kFinalizeVerify) a.committed[row] = -1;
+    if (lane == 0) {
+      if (a.kind == kFinalizeVerify) a.n_accepted[b] = -1;
+      if (a.flags) a.flags[b] = JSV_FLAG_INVALID;
+      ReqState rq{}; rq.k = -1; rq.flags = JSV_FLAG_INVALID; a.req[b] = rq;
+    }
+    if (a.kind == kFinalizeScore) {
+      if (lane < a.top_n) {
+        a.out_len[b * a.top_n + lane] = -1;
+        a.out_token[b * a.top_n + lane] = -1;
+        a.out_prob[b * a.top_n + lane] = 0.f;
+      }
+      if (act && a.len_marginal) a.len_marginal[row] = 0.0;
+    }
+    return;
+  }
+
+  double alpha = 0.0;
+  if (!soft) {
+    // Greedy verification: accept while the draft equals the row's argmax.
+    alpha = (lane < K && di == st.idx) ? 1.0 : 0.0;
+  } else if (lane < K) {
+    const double pd = exp2((zd_sh[lane] - double(st.m)) * cd) / st.s;
+    if (a.mode == JSV_PROPOSAL_POINT) {
+      alpha = pd;
+    } else {
+      const double gd = a.G[(size_t)(b * K + lane) * V + di];
+      const double qd = exp2((gd - double(st.mq)) * cd) / st.sq;
+      alpha = (pd == 0.0) ? 0.0 : (pd >= qd ? 1.0 : pd / qd);
+    }
+  }
+
+  uint32_t f = 0;
+  int k = K;
+  double vk = 0.0;
+  if (!soft) {
+    const uint64_t rej = __ballot(lane < K && alpha == 0.0);
+    k = rej ? __builtin_ctzll(rej) : K;
+    const bool gap = act && lane <= k && (st.m - st.top2) < kLogitGapTie;
+    if (__ballot(gap)) f |= JSV_FLAG_LOGIT_GAP;
+  } else if (a.kind == kFinalizeVerify) {
+    double u = 0.0, v = 0.0;
+    if (act) row_uniforms(a.seed, a.offset, b, lane, u, v);
+    const uint64_t rej = __ballot(lane < K && !(u < alpha));
+    k = rej ? __builtin_ctzll(rej) : K;
+    const bool tie = lane < K && lane <= k && fabs(u - alpha) < kAcceptTie;
+    if (__ballot(tie)) f |= JSV_FLAG_ACCEPT_TIE;
+    vk = __shfl(v, k);
+  }
+  const int bonus = __shfl(st.idx, k);
+
+  // A_i = prod_{j<i} alpha_j (probability of reaching row i).
+  double A = 1.0;
+  for (int j = 0; j < K; ++j) {
+    const double aj = __shfl(alpha, j);
+    if (j < lane) A *= aj;
+  }
+
+  if (act) {
+    RowFinal rf{};
+    rf.s = st.s; rf.sq = st.sq; rf.alpha = alpha; rf.A = A;
+    rf.m = st.m; rf.top2 = st.top2; rf.mq = st.mq; rf.idx = st.idx; rf.flags = st.flags;
+    a.rowfinal[row] = rf;
+  }
+  if (a.kind == kFinalizeVerify) {
+    if (act) a.committed[row] = (lane < k) ? di : ((lane == k && !soft) ? bonus : -1);
+    if (lane == 0) {
+      a.n_accepted[b] = k;
+      if (a.flags) a.flags[b] = f;
+      ReqState rq{}; rq.vk = vk; rq.k = k; rq.flags = f; a.req[b] = rq;
+    }
+  } else {  // score
+    if (act && a.len_marginal) {
+      a.len_marginal[row] = soft ? ((lane < K) ? A * (1.0 - alpha) : A) : (lane == k ? 1.0 : 0.0);
+    }
+    if (!soft && lane < a.top_n) {  // all mass on the greedy outcome
+      a.out_len[b * a.top_n + lane] = (lane == 0) ? k : -1;
+      a.out_token[b * a.top_n + lane] = (lane == 0) ? bonus : -1;
+      a.out_prob[b * a.top_n + lane] = (lane == 0) ? 1.f : 0.f;
+    }
+    if (lane == 0) {
+      if (a.flags) a.flags[b] = f;
+      ReqState rq{}; rq.k = k; rq.flags = f; a.req[b] = rq;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -671,113 +743,99 @@ struct RowModel {
   }
 };
 
+__device__ inline RowModel row_model(const RowFinal& rf, float c, int mode, int k, int K, int dk) {
+  RowModel rm;
+  rm.m = rf.m; rm.mq = rf.mq; rm.c = c; rm.s = rf.s; rm.sq = rf.sq;
+  rm.use_q = (mode == JSV_PROPOSAL_SOFTMAX) && k < K;
+  rm.dk = (mode == JSV_PROPOSAL_POINT && k < K) ? dk : -1;
+  return rm;
+}
+
 // ------------------------------------------------------------------------------------
-// Bonus sampler: grid (slices, B).  Each slice sums the residual of row k over its
-// columns; the last slice of a request locates t = v_k * Z in the slice totals, then
-// re-walks that slice with a block prefix sum to the first column whose CDF exceeds t.
-__global__ __launch_bounds__(kSliceThreads) void sample_kernel(SampleArgs a) {
+// Bonus sampler, part 1: grid (slices, B).  Residual mass (and target mass, for the
+// zero-residual fallback) of row k over each vocabulary slice.
+__global__ __launch_bounds__(kSliceThreads) void slice_sum_kernel(SampleArgs a) {
   const int b = blockIdx.y, j = blockIdx.x, NB = gridDim.x, tid = threadIdx.x;
   const ReqState rq = a.req[b];
   if (!(a.T > 0.f) || rq.k < 0) return;
   const int K = a.K, k = rq.k, row = b * (K + 1) + k;
-  const RowFinal rf = a.rowfinal[row];
-  const int64_t V = a.V;
-  const float* zr = a.logits + (size_t)row * V;
-  RowModel rm;
-  rm.m = rf.m; rm.mq = rf.mq; rm.c = a.c; rm.s = rf.s; rm.sq = rf.sq;
-  rm.use_q = (a.mode == JSV_PROPOSAL_SOFTMAX) && k < K;
-  rm.dk = (a.mode == JSV_PROPOSAL_POINT && k < K) ? a.drafts[b * K + k] : -1;
-  const float* gr = rm.use_q ? a.G + (size_t)(b * K + k) * V : nullptr;
-  const int64_t L = (V + NB - 1) / NB;
+  const RowModel rm = row_model(a.rowfinal[row], a.c, a.mode, k, K, k < K ? a.drafts[b * K + k] : -1);
+  const int64_t V = a.V, L = (V + NB - 1) / NB, v0 = (int64_t)j * L;
+  const int n = (int)max<int64_t>(0, min<int64_t>(V, v0 + L) - v0);
+  const float* zr = a.logits + (size_t)row * V + v0;
+  const float* gr = rm.use_q ? a.G + (size_t)(b * K + k) * V + v0 : nullptr;
+  __shared__ double dsh[8];
+  double rs = 0.0, ps = 0.0;
+  for (int e = tid; e < n; e += kSliceThreads) {
+    double r, p;
+    rm.eval(v0 + e, zr[e], gr ? gr[e] : 0.f, r, p);
+    rs += r;
+    ps += p;
+  }
+  rs = block_sum(rs, dsh);
+  ps = block_sum(ps, dsh);
+  if (tid == 0) {
+    a.zs[((size_t)b * NB + j) * 2 + 0] = rs;
+    a.zs[((size_t)b * NB + j) * 2 + 1] = ps;
+  }
+}
 
+// Bonus sampler, part 2: grid (B).  Locate t = v_k * Z among the slice totals, then walk
+// that slice with a block prefix sum to the first column whose CDF exceeds t.
+__global__ __launch_bounds__(kSliceThreads) void locate_kernel(SampleArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, NB = sample_slices(a.V);
+  const ReqState rq = a.req[b];
+  if (!(a.T > 0.f) || rq.k < 0) return;
+  const int K = a.K, k = rq.k, row = b * (K + 1) + k;
+  const RowModel rm = row_model(a.rowfinal[row], a.c, a.mode, k, K, k < K ? a.drafts[b * K + k] : -1);
+  const int64_t V = a.V, L = (V + NB - 1) / NB;
   __shared__ float zsh[kSampleMaxSlice];
   __shared__ float gsh[kSampleMaxSlice];
   __shared__ double dsh[8];
   __shared__ int ish[8];
-  __shared__ uint32_t last_flag;
-  __shared__ double bc_t, bc_base, bc_Z, bc_clo, bc_chi;
-  __shared__ int bc_s, bc_zero, bc_fall;
+  __shared__ double bc_base, bc_clo, bc_chi;
 
-  auto stage = [&](int64_t v0, int n) {
-    for (int e = tid; e < n; e += kSliceThreads) {
-      zsh[e] = zr[v0 + e];
-      if (gr) gsh[e] = gr[v0 + e];
-    }
-    __syncthreads();
-  };
-
-  {
-    const int64_t v0 = (int64_t)j * L;
-    const int n = (int)max<int64_t>(0, min<int64_t>(V, v0 + L) - v0);
-    stage(v0, n);
-    const int E = (n + kSliceThreads - 1) / kSliceThreads;
-    const int e0 = tid * E, e1 = min(n, e0 + E);
-    double rs = 0.0, ps = 0.0;
-    for (int e = e0; e < e1; ++e) {
-      double r, p;
-      rm.eval(v0 + e, zsh[e], gr ? gsh[e] : 0.f, r, p);
-      rs += r;
-      ps += p;
-    }
-    rs = block_sum(rs, dsh);
-    ps = block_sum(ps, dsh);
-    if (tid == 0) {
-      a.zs[((size_t)b * NB + j) * 2 + 0] = rs;
-      a.zs[((size_t)b * NB + j) * 2 + 1] = ps;
-    }
+  // slice totals: each thread owns a contiguous run of slices
+  const double* zsb = a.zs + (size_t)b * NB * 2;
+  const int SE = (NB + kSliceThreads - 1) / kSliceThreads;
+  const int q0 = tid * SE, q1 = min(NB, q0 + SE);
+  double xr = 0.0, xp = 0.0;
+  for (int q = q0; q < q1; ++q) { xr += zsb[2 * q]; xp += zsb[2 * q + 1]; }
+  const double Zr = block_sum(xr, dsh);
+  const double Zp = block_sum(xp, dsh);
+  const int zero = (Zr > 0.0) ? 0 : 1;
+  const double Z = zero ? Zp : Zr;
+  const double t = rq.vk * Z;
+  double cb = block_exclusive_scan(zero ? xp : xr, dsh);
+  const double cb0 = cb;
+  int cand = INT_MAX, lastnz = -1;
+  double cbase = 0.0;
+  for (int q = q0; q < q1; ++q) {
+    const double x = zsb[2 * q + zero];
+    if (x > 0.0) lastnz = q;
+    if (cand == INT_MAX && x > 0.0 && cb + x > t) { cand = q; cbase = cb; }
+    cb += x;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last_flag = (atomicAdd(&a.counter[b], 1u) == uint32_t(NB - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-
-  uint32_t f = 0;
-  {
-    // Locate the slice holding t = v_k * Z: block sums and an exclusive scan over the
-    // slice totals (each thread owns a contiguous run of slices), then the first slice
-    // whose cumulative mass exceeds t.
-    const double* zsb = a.zs + (size_t)b * NB * 2;
-    const int SE = (NB + kSliceThreads - 1) / kSliceThreads;
-    const int q0 = tid * SE, q1 = min(NB, q0 + SE);
-    double xr = 0.0, xp = 0.0;
-    for (int q = q0; q < q1; ++q) { xr += zsb[2 * q]; xp += zsb[2 * q + 1]; }
-    const double Zr = block_sum(xr, dsh);
-    const double Zp = block_sum(xp, dsh);
-    const int zero = (Zr > 0.0) ? 0 : 1;
-    const double Z = zero ? Zp : Zr;
-    const double t = rq.vk * Z;
-    double cb = block_exclusive_scan(zero ? xp : xr, dsh);
-    int cand = INT_MAX, lastnz = -1;
-    double cbase = 0.0;
-    for (int q = q0; q < q1; ++q) {
-      const double x = zsb[2 * q + zero];
-      if (x > 0.0) lastnz = q;
-      if (cand == INT_MAX && x > 0.0 && cb + x > t) { cand = q; cbase = cb; }
-      cb += x;
-    }
-    const int sfound = block_min_int(cand, ish);
-    const int slast = block_max_int(lastnz, ish);
-    if (sfound != INT_MAX && cand == sfound) bc_base = cbase;
-    if (sfound == INT_MAX) {  // rounding left t at or above the last CDF value
-      double c2 = block_exclusive_scan(zero ? xp : xr, dsh);
-      for (int q = q0; q < q1 && q < slast; ++q) c2 += zsb[2 * q + zero];
-      if (q0 <= slast && slast < q1) bc_base = c2;
-    }
-    if (tid == 0) {
-      bc_t = t; bc_Z = Z; bc_zero = zero;
-      bc_s = (sfound != INT_MAX) ? sfound : (slast >= 0 ? slast : 0);
-      bc_fall = (sfound == INT_MAX) ? 1 : 0;
-    }
+  const int sfound = block_min_int(cand, ish);
+  const int slast = block_max_int(lastnz, ish);
+  const int fall = (sfound == INT_MAX) ? 1 : 0;   // rounding left t at or above the last CDF value
+  const int s = fall ? (slast >= 0 ? slast : 0) : sfound;
+  if (!fall && cand == sfound) bc_base = cbase;
+  if (fall && q0 <= s && s < q1) {
+    double c2 = cb0;
+    for (int q = q0; q < s; ++q) c2 += zsb[2 * q + zero];
+    bc_base = c2;
   }
-  __syncthreads();
-  const int s = bc_s, zero = bc_zero;
-  const double t = bc_t, Z = bc_Z;
-  if (zero) f |= JSV_FLAG_ZERO_RESIDUAL;
+  // stage slice s
   const int64_t v0 = (int64_t)s * L;
   const int n = (int)max<int64_t>(0, min<int64_t>(V, v0 + L) - v0);
-  stage(v0, n);
+  const float* zr = a.logits + (size_t)row * V;
+  const float* gr = rm.use_q ? a.G + (size_t)(b * K + k) * V : nullptr;
+  for (int e = tid; e < n; e += kSliceThreads) {
+    zsh[e] = zr[v0 + e];
+    if (gr) gsh[e] = gr[v0 + e];
+  }
+  __syncthreads();
   const int E = (n + kSliceThreads - 1) / kSliceThreads;
   const int e0 = tid * E, e1 = min(n, e0 + E);
   double mine = 0.0;
@@ -803,7 +861,8 @@ __global__ __launch_bounds__(kSliceThreads) void sample_kernel(SampleArgs a) {
   const int lastp = block_max_int(last_pos, ish);
   __syncthreads();
   if (tid == 0) {
-    if (tok == INT_MAX || bc_fall) {
+    uint32_t f = zero ? JSV_FLAG_ZERO_RESIDUAL : 0u;
+    if (tok == INT_MAX || fall) {
       tok = lastp;
       f |= JSV_FLAG_CDF_TIE;
     } else if ((t - bc_clo) < kCdfTie * Z || (bc_chi - t) < kCdfTie * Z) {
@@ -811,14 +870,12 @@ __global__ __launch_bounds__(kSliceThreads) void sample_kernel(SampleArgs a) {
     }
     a.committed[row] = tok;
     if (a.flags) a.flags[b] |= f;
-    a.counter[b] = 0u;
   }
 }
 
 // ------------------------------------------------------------------------------------
-// Outcome scorer: grid (slices, K+1, B).  Each (row k, slice) computes its residual mass
-// and its top-(N+1) columns by (r desc, p desc, token asc); the last workgroup of a
-// request turns candidates into P(k, a) and selects the top-N by (P desc, k asc, a asc).
+// Outcome scorer, part 1: grid (slices, K+1, B).  Residual mass of (row k, slice) and its
+// top-(N+1) columns by (r desc, p desc, token asc).
 struct Key {
   double r, p;
   int v;
@@ -846,7 +903,7 @@ __device__ inline Key block_best(Key k, Key* sh) {
   return best;
 }
 
-__global__ __launch_bounds__(kSliceThreads) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kSliceThreads) void score_slice_kernel(ScoreArgs a) {
   const int b = blockIdx.z, k = blockIdx.y, j = blockIdx.x, NB = gridDim.x, tid = threadIdx.x;
   const ReqState rq = a.req[b];
   if (!(a.T > 0.f) || rq.k < 0) return;
@@ -854,10 +911,7 @@ __global__ __launch_bounds__(kSliceThreads) void score_kernel(ScoreArgs a) {
   const RowFinal rf = a.rowfinal[row];
   const int64_t V = a.V;
   const double Pk = (k < K) ? rf.A * (1.0 - rf.alpha) : rf.A;
-  RowModel rm;
-  rm.m = rf.m; rm.mq = rf.mq; rm.c = a.c; rm.s = rf.s; rm.sq = rf.sq;
-  rm.use_q = (a.mode == JSV_PROPOSAL_SOFTMAX) && k < K;
-  rm.dk = (a.mode == JSV_PROPOSAL_POINT && k < K) ? a.drafts[b * K + k] : -1;
+  const RowModel rm = row_model(rf, a.c, a.mode, k, K, k < K ? a.drafts[b * K + k] : -1);
   const float* zr = a.logits + (size_t)row * V;
   const float* gr = rm.use_q ? a.G + (size_t)(b * K + k) * V : nullptr;
   const int64_t L = (V + NB - 1) / NB;
@@ -868,63 +922,60 @@ __global__ __launch_bounds__(kSliceThreads) void score_kernel(ScoreArgs a) {
   __shared__ double psh[kScoreMaxSlice];
   __shared__ double dsh[8];
   __shared__ Key ksh[8];
-  __shared__ uint32_t last_flag;
 
   Cand* cand = a.cand + ((size_t)row * NB + j) * N1;
-  if (Pk > 0.0) {
-    for (int e = tid; e < n; e += kSliceThreads) {
-      double r, p;
-      rm.eval(v0 + e, zr[v0 + e], gr ? gr[v0 + e] : 0.f, r, p);
-      rsh[e] = r;
-      psh[e] = p;
-    }
-    __syncthreads();
-    const int E = (n + kSliceThreads - 1) / kSliceThreads;
-    const int e0 = tid * E, e1 = min(n, e0 + E);
-    double rs = 0.0;
-    for (int e = e0; e < e1; ++e) rs += rsh[e];
-    rs = block_sum(rs, dsh);
-    if (tid == 0) a.zs[(size_t)row * NB + j] = rs;
-    Key thr{INFINITY, INFINITY, -1};
-    for (int q = 0; q < N1; ++q) {
-      Key best{-1.0, -1.0, INT_MAX};
-      for (int e = e0; e < e1; ++e) {
-        const Key x{rsh[e], psh[e], int(v0 + e)};
-        if (key_better(thr, x) && key_better(x, best)) best = x;
-      }
-      best = block_best(best, ksh);
-      if (tid == 0) {
-        Cand cd{};
-        cd.r = best.r; cd.p = best.p; cd.tok = (best.v == INT_MAX) ? -1 : best.v;
-        cand[q] = cd;
-      }
-      thr = best;
-    }
-  } else {
+  if (!(Pk > 0.0)) {  // the row contributes no outcome
     if (tid == 0) a.zs[(size_t)row * NB + j] = 0.0;
     for (int q = tid; q < N1; q += kSliceThreads) {
       Cand cd{};
       cd.r = -1.0; cd.p = -1.0; cd.tok = -1;
       cand[q] = cd;
     }
+    return;
   }
-
-  __threadfence();
+  for (int e = tid; e < n; e += kSliceThreads) {
+    double r, p;
+    rm.eval(v0 + e, zr[v0 + e], gr ? gr[v0 + e] : 0.f, r, p);
+    rsh[e] = r;
+    psh[e] = p;
+  }
   __syncthreads();
-  if (tid == 0) last_flag = (atomicAdd(&a.counter[b], 1u) == uint32_t(R * NB - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
+  const int E = (n + kSliceThreads - 1) / kSliceThreads;
+  const int e0 = tid * E, e1 = min(n, e0 + E);
+  double rs = 0.0;
+  for (int e = e0; e < e1; ++e) rs += rsh[e];
+  rs = block_sum(rs, dsh);
+  if (tid == 0) a.zs[(size_t)row * NB + j] = rs;
+  Key thr{INFINITY, INFINITY, -1};
+  for (int q = 0; q < N1; ++q) {
+    Key best{-1.0, -1.0, INT_MAX};
+    for (int e = e0; e < e1; ++e) {
+      const Key x{rsh[e], psh[e], int(v0 + e)};
+      if (key_better(thr, x) && key_better(x, best)) best = x;
+    }
+    best = block_best(best, ksh);
+    if (tid == 0) {
+      Cand cd{};
+      cd.r = best.r; cd.p = best.p; cd.tok = (best.v == INT_MAX) ? -1 : best.v;
+      cand[q] = cd;
+    }
+    thr = best;
+  }
+}
 
-  // Merge: scale_k turns a candidate of row k into P(k, a).
+// Outcome scorer, part 2: grid (B).  Residual mass per row, then P(k, a) of every
+// candidate and the top-N by (P desc, k asc, a asc).
+__global__ __launch_bounds__(kSliceThreads) void score_merge_kernel(ScoreArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, NB = score_slices(a.V);
+  const ReqState rq = a.req[b];
+  if (!(a.T > 0.f) || rq.k < 0) return;
+  const int K = a.K, R = K + 1, N1 = a.top_n + 1;
   __shared__ double scale_sh[kMaxK + 1];
   __shared__ double zk_sh[kMaxK + 1];
   __shared__ int usep_sh[kMaxK + 1];
   __shared__ uint32_t flag_sh;
+  __shared__ Key ksh[8];
   if (tid == 0) flag_sh = 0u;
-  __syncthreads();
-  // Residual mass of row kk: wave kk % 4 sums its slice totals (fixed order per lane,
-  // then a fixed shuffle tree).
   {
     const int w = tid >> 6, lane = tid & 63;
     for (int kk = w; kk < R; kk += kSliceThreads / kWave) {
@@ -953,8 +1004,7 @@ __global__ __launch_bounds__(kSliceThreads) void score_kernel(ScoreArgs a) {
 
   const int total = R * NB * N1;
   const Cand* cb = a.cand + (size_t)b * R * NB * N1;
-  // Key for the merge: r := P, p := -row, v := token (so "better" = larger P, then
-  // smaller row, then smaller token).
+  // Merge key: r := P, p := -row, v := token (larger P, then smaller row, then smaller token).
   Key thr{INFINITY, INFINITY, -1};
   double prev = -1.0;
   for (int q = 0; q < N1; ++q) {
@@ -982,10 +1032,7 @@ __global__ __launch_bounds__(kSliceThreads) void score_kernel(ScoreArgs a) {
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    if (a.flags) a.flags[b] |= flag_sh;
-    a.counter[b] = 0u;
-  }
+  if (tid == 0 && a.flags) a.flags[b] |= flag_sh;
 }
 
 // ------------------------------------------------------------------------------------
@@ -1018,10 +1065,11 @@ static hipError_t dispatch_nks(int nks, int grid, const StatsArgs& a, hipStream_
   }
 }
 
-// Tiling of `rows` (1..33) tokens: full 16-token MFMA tiles, and one leftover row on
-// the VALU when exactly one row is left over.
+// Tiling of `rows` (1..33) tokens: full 16-token MFMA tiles, plus one row on the VALU
+// when exactly one row is left over.
 template <int DT>
-static hipError_t dispatch_rows(int rows, int nks, int grid, const StatsArgs& a, hipStream_t s) {
+static hipError_t dispatch_rows(int nks, int grid, const StatsArgs& a, hipStream_t s) {
+  const int rows = a.rows;
   if (rows <= 1) return dispatch_nks<DT, 0, 1>(nks, grid, a, s);
   if (rows <= 16) return dispatch_nks<DT, 1, 0>(nks, grid, a, s);
   if (rows == 17) return dispatch_nks<DT, 1, 1>(nks, grid, a, s);
@@ -1029,22 +1077,32 @@ static hipError_t dispatch_rows(int rows, int nks, int grid, const StatsArgs& a,
   return dispatch_nks<DT, 2, 1>(nks, grid, a, s);
 }
 
-hipError_t launch_stats(int dtype, int nks, int rows, int grid, const StatsArgs& a,
-                        hipStream_t stream) {
-  if (rows < 1 || rows > kRowsPerPass) return hipErrorInvalidValue;
-  return dtype == JSV_BF16 ? dispatch_rows<JSV_BF16>(rows, nks, grid, a, stream)
-                           : dispatch_rows<JSV_F32>(rows, nks, grid, a, stream);
+hipError_t launch_stats(int dtype, int nks, int grid, const StatsArgs& a, hipStream_t stream) {
+  if (a.rows < 1 || a.rows > kRowsPerPass) return hipErrorInvalidValue;
+  return dtype == JSV_BF16 ? dispatch_rows<JSV_BF16>(nks, grid, a, stream)
+                           : dispatch_rows<JSV_F32>(nks, grid, a, stream);
+}
+
+hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(a.B), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(sample_kernel, dim3(sample_slices(a.V), a.B), dim3(kSliceThreads), 0,
+  hipLaunchKernelGGL(slice_sum_kernel, dim3(sample_slices(a.V), a.B), dim3(kSliceThreads), 0,
                      stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(locate_kernel, dim3(a.B), dim3(kSliceThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(score_kernel, dim3(score_slices(a.V), a.K + 1, a.B), dim3(kSliceThreads),
-                     0, stream, a);
+  hipLaunchKernelGGL(score_slice_kernel, dim3(score_slices(a.V), a.K + 1, a.B),
+                     dim3(kSliceThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(score_merge_kernel, dim3(a.B), dim3(kSliceThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.jsv_verify_block.restype = i32
     lib.jsv_verify_stats.argtypes = verify_args
     lib.jsv_verify_stats.restype = i32
-    lib.jsv_verify_sample.argtypes = [hp, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]
+    lib.jsv_verify_sample.argtypes = verify_args
     lib.jsv_verify_sample.restype = i32
     lib.jsv_score_outcomes.argtypes = [hp, vp, vp, vp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp,
                                        vp, sz, vp]
@@ -134,8 +134,8 @@ def workspace_bytes(head: LMHead, batch: int, K: int, top_n: int = 0) -> int:
 
 
 def new_workspace(head: LMHead, batch: int, K: int, top_n: int = 0) -> torch.Tensor:
-    """A zero-filled device workspace big enough for (batch, K, top_n)."""
-    return torch.zeros(workspace_bytes(head, batch, K, top_n), dtype=torch.uint8, device=head.device)
+    """A device workspace big enough for (batch, K, top_n)."""
+    return torch.empty(workspace_bytes(head, batch, K, top_n), dtype=torch.uint8, device=head.device)
 
 
 def lmhead_logits(head: LMHead, hidden: torch.Tensor, out: torch.Tensor | None = None, stream=None):
@@ -201,21 +201,16 @@ def verify_block(head, hidden, draft_tokens, draft_logits, temperature, mode, se
 
 def verify_stats(head, hidden, draft_tokens, draft_logits, temperature, mode, seed, offset,
                  workspace, out=None, logits_out=None, stream=None) -> VerifyOut:
-    """jsv_verify_stats: first half of verify_block (norm, LM head, statistics, scan)."""
+    """jsv_verify_stats: first half of verify_block (RMSNorm, LM head, statistics)."""
     return _verify_call(load_library().jsv_verify_stats, head, hidden, draft_tokens, draft_logits,
                         temperature, mode, seed, offset, workspace, out, logits_out, stream)
 
 
-def verify_sample(head, draft_tokens, draft_logits, temperature, mode, workspace, out,
-                  logits_out=None, stream=None) -> VerifyOut:
-    """jsv_verify_sample: second half of verify_block (bonus token)."""
-    B, K = _block_checks(head, None, draft_tokens, draft_logits, mode, temperature)
-    _need(workspace, "workspace", torch.uint8, device=head.device)
-    _check(load_library().jsv_verify_sample(
-        ctypes.byref(head._c), _ptr(draft_tokens), _ptr(draft_logits), B, K, float(temperature),
-        int(mode), _ptr(out.committed), _ptr(out.flags), _ptr(logits_out), _ptr(workspace),
-        workspace.numel(), _stream(stream)))
-    return out
+def verify_sample(head, hidden, draft_tokens, draft_logits, temperature, mode, seed, offset,
+                  workspace, out=None, logits_out=None, stream=None) -> VerifyOut:
+    """jsv_verify_sample: second half of verify_block (acceptance scan, bonus token)."""
+    return _verify_call(load_library().jsv_verify_sample, head, hidden, draft_tokens, draft_logits,
+                        temperature, mode, seed, offset, workspace, out, logits_out, stream)
 
 
 class ScoreOut:

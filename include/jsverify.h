@@ -12,10 +12,9 @@
  * Conventions for every call
  *   - Pointers named as device pointers are contiguous row-major device memory owned
  *     by the caller.  The library never allocates device memory.
- *   - `ws` is a caller-owned device workspace of at least jsv_workspace_bytes() bytes.
- *     It must be zero-filled once before its first use (hipMemset after allocation);
- *     every call that completes leaves its counter area zero again.  Two calls that
- *     overlap in time must not share a workspace.
+ *   - `ws` is a caller-owned device workspace of at least jsv_workspace_bytes() bytes
+ *     (16-byte aligned, contents need no initialisation).  Two calls that overlap in
+ *     time must not share a workspace.
  *   - Calls enqueue kernels on `hip_stream` (a hipStream_t; NULL = the null stream)
  *     and return without synchronising.  Outputs are valid once the stream reaches
  *     the end of the call.
@@ -33,8 +32,8 @@
  *     word x0 gives u_i = x0 * 2^-32 for the acceptance test of row i, words x1, x2
  *     give v_i = (x1 * 2^21 + (x2 >> 11)) * 2^-53 for a bonus drawn at row i.
  *   - Supported shapes: hidden / 256 (bf16) or hidden / 128 (f32) in {1, 2, 4, 8, 12, 16, 20}
- *     (so d = 4096 and 5120 for bf16); 1 <= vocab <= 2^31 - 1; 1 <= K <= 32;
- *     1 <= B <= 8.  Anything else returns JSV_EUNSUPPORTED or JSV_EINVAL.
+ *     (so d = 4096 and 5120 for bf16); 1 <= vocab <= 2^22; 1 <= K <= 32; 1 <= B <= 8.
+ *     Anything else returns JSV_EUNSUPPORTED or JSV_EINVAL.
  */
 #ifndef JSVERIFY_H
 #define JSVERIFY_H
@@ -115,22 +114,24 @@ jsv_status jsv_verify_block(const jsv_lm_head* head, const void* hidden,
                             float* logits_out, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* The two halves of jsv_verify_block, for callers that want to time or interleave them.
-   jsv_verify_stats runs the fused RMSNorm + LM head + per-row softmax statistics and the
-   acceptance scan; it writes n_accepted, the accepted prefix of `committed`, the -1
-   padding and the flags.  jsv_verify_sample then draws the bonus token.  Call them in
-   this order on one stream with the same arguments and workspace.  At T = 0 the bonus
-   is already written by jsv_verify_stats and jsv_verify_sample only returns. */
+   jsv_verify_stats runs the fused RMSNorm + LM head with its per-row softmax statistics
+   (one stream over W; writes the logits and statistics into logits_out / ws only).
+   jsv_verify_sample then runs the acceptance scan and draws the bonus token, writing
+   n_accepted, committed and flags.  Call them in this order on one stream with the same
+   arguments and workspace; jsv_verify_block is exactly the two in sequence. */
 jsv_status jsv_verify_stats(const jsv_lm_head* head, const void* hidden,
                             const int32_t* draft_tokens, const float* draft_logits,
                             int32_t B, int32_t K, float temperature, int32_t mode,
                             uint64_t seed, uint64_t offset,
                             int32_t* n_accepted, int32_t* committed, uint32_t* flags,
                             float* logits_out, void* ws, size_t ws_bytes, void* hip_stream);
-jsv_status jsv_verify_sample(const jsv_lm_head* head, const int32_t* draft_tokens,
-                             const float* draft_logits, int32_t B, int32_t K,
-                             float temperature, int32_t mode,
-                             int32_t* committed, uint32_t* flags, const float* logits_out,
-                             void* ws, size_t ws_bytes, void* hip_stream);
+jsv_status jsv_verify_sample(const jsv_lm_head* head, const void* hidden,
+                             const int32_t* draft_tokens, const float* draft_logits,
+                             int32_t B, int32_t K, float temperature, int32_t mode,
+                             uint64_t seed, uint64_t offset,
+                             int32_t* n_accepted, int32_t* committed, uint32_t* flags,
+                             const float* logits_out, void* ws, size_t ws_bytes,
+                             void* hip_stream);
 
 /* Foresight outcome scoring (paper §4.2 Eq. 6 and Eq. 7; App. B.1).
    hidden_pred: device [B][K+1][hidden], predicted states of the block under verification.

@@ -232,7 +232,7 @@ def test_stages_equal_block_and_runs_are_bit_identical(qwen, dev):
         o = jsv.verify_block(qwen.gpu, h, d, g, 1.0, SOFT, 9, rep % 2, ws, logits_out=lo)
         outs.append((o, lo))
     o2 = jsv.verify_stats(qwen.gpu, h, d, g, 1.0, SOFT, 9, 0, ws)
-    jsv.verify_sample(qwen.gpu, d, g, 1.0, SOFT, ws, o2)
+    jsv.verify_sample(qwen.gpu, h, d, g, 1.0, SOFT, 9, 0, ws, out=o2)
     torch.cuda.synchronize()
     assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][1], outs[2][1])
     assert torch.equal(outs[0][0].committed, outs[2][0].committed)
