@@ -112,6 +112,8 @@ FinalArgs final_args(const jsv_lm_head* head, const void* hidden, const int32_t*
   f.kind = kind;
   f.P = stats_grid(head->vocab);
   f.partial = reinterpret_cast<const RowStat*>(ws + L.partial);
+  f.rowstat = reinterpret_cast<RowStat*>(ws + L.rowstat);
+  f.dlog = reinterpret_cast<DraftLogit*>(ws + L.dlog);
   f.rnorm = reinterpret_cast<const float*>(ws + L.rnorm);
   f.rowfinal = reinterpret_cast<RowFinal*>(ws + L.rowfinal);
   f.req = reinterpret_cast<ReqState*>(ws + L.req);
@@ -235,8 +237,6 @@ jsv_status jsv_verify_sample(const jsv_lm_head* head, const void* hidden,
   a.mode = mode;
   a.logits = logits_out ? logits_out : reinterpret_cast<const float*>(w + L.logits);
   a.G = draft_logits;
-  a.drafts = draft_tokens;
-  a.rowfinal = reinterpret_cast<const RowFinal*>(w + L.rowfinal);
   a.req = reinterpret_cast<const ReqState*>(w + L.req);
   a.zs = reinterpret_cast<double*>(w + L.zs);
   a.committed = committed;

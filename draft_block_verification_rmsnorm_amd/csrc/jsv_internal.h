@@ -13,27 +13,29 @@ constexpr int kWaves = 8;                  // waves per workgroup of the LM-head
 constexpr int kThreads = kWaves * kWave;   // 512
 constexpr int kRowsPerPass = 33;           // two 16-token MFMA tiles + one VALU row per pass over W
 constexpr int kMaxGrid = 1024;             // LM-head workgroups (= partial records per row)
-constexpr int kSampleSlices = 64;          // vocabulary slices of the bonus sampler
 constexpr int kScoreSlices = 64;           // vocabulary slices per row of the scorer
 constexpr int kSliceThreads = 256;
+constexpr int kSampleCols = 4;             // columns per thread of the bonus sampler
+constexpr int kSampleSlice = kSliceThreads * kSampleCols;  // columns per sampler slice
 constexpr int kMaxB = 8;
 constexpr int kMaxK = 32;
 constexpr int kMaxTopN = 64;
-constexpr int kSampleMaxSlice = 4096;      // columns staged in LDS by one sampler workgroup
 constexpr int kScoreMaxSlice = 2048;       // columns staged in LDS by one scorer workgroup
 constexpr int64_t kMaxVocab = int64_t(1) << 22;
 
-// Per (LM-head workgroup, row) partial statistics of the logits and draft logits.
+// Per (row, LM-head workgroup) partial statistics of the logits and draft logits,
+// stored row-major: partial[row * P + workgroup].
 struct alignas(16) RowStat {
   double s;        // sum over this workgroup's columns of exp((z - m) / T)       (T > 0)
   double sq;       // same for the draft logits of this row (draft rows, softmax, T > 0)
   float m;         // max logit
   float top2;      // second largest logit (equal to m when the max is shared)
   float mq;        // max draft logit
-  int idx;         // argmax, lowest token id among equal maxima
-  uint32_t flags;  // JSV_FLAG_INVALID when a non-finite logit or draft logit was seen
-  int pad[3];
+  uint32_t idxf;   // argmax (lowest token id among equal maxima) in bits 0..30; bit 31 set
+                   // when a non-finite logit or draft logit was seen
 };
+constexpr uint32_t kIdxMask = 0x7fffffffu;
+constexpr uint32_t kBadBit = 0x80000000u;
 
 // Per-row statistics after combining every workgroup's partial.
 struct alignas(16) RowFinal {
@@ -46,12 +48,23 @@ struct alignas(16) RowFinal {
   int pad[3];
 };
 
-// Per-request result of the acceptance scan, read by the bonus sampler and scorer.
+// Float64 logit of a draft row at its draft token, and the draft logit there.
+struct alignas(16) DraftLogit {
+  double z;
+  float g;
+  int pad;
+};
+
+// Per-request result of the acceptance scan, read by the bonus sampler and scorer,
+// with the statistics of row k that the residual there needs.
 struct alignas(16) ReqState {
   double vk;       // bonus uniform of row k
+  double s, sq;    // softmax normalisers of row k (logits, draft logits)
+  float m, mq;     // maxima of row k
   int k;           // first rejection (K if none); -1 for an invalid request
+  int dk;          // point-mass proposal: the draft token removed from the residual, else -1
+  int use_q;       // residual max(p - q, 0) with the softmax proposal q of row k
   uint32_t flags;
-  int pad[4];
 };
 
 // One top-N candidate of a (request, row, slice) of the scorer.
@@ -63,8 +76,7 @@ struct alignas(8) Cand {
 };
 
 __host__ __device__ inline int sample_slices(int64_t V) {
-  const int64_t need = (V + kSampleMaxSlice - 1) / kSampleMaxSlice;
-  return int(need > kSampleSlices ? need : kSampleSlices);
+  return int((V + kSampleSlice - 1) / kSampleSlice);
 }
 __host__ __device__ inline int score_slices(int64_t V) {
   const int64_t need = (V + kScoreMaxSlice - 1) / kScoreMaxSlice;
@@ -72,7 +84,7 @@ __host__ __device__ inline int score_slices(int64_t V) {
 }
 
 struct WsLayout {
-  size_t req, rowfinal, rnorm, partial, zs, cand, logits, total;
+  size_t req, rowfinal, rowstat, dlog, rnorm, partial, zs, cand, logits, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -84,6 +96,8 @@ inline WsLayout ws_layout(int64_t V, int B, int K, int top_n) {
   size_t off = 0;
   L.req = off;      off = align256(off + kMaxB * sizeof(ReqState));
   L.rowfinal = off; off = align256(off + M * sizeof(RowFinal));
+  L.rowstat = off;  off = align256(off + M * sizeof(RowStat));
+  L.dlog = off;     off = align256(off + M * sizeof(DraftLogit));
   L.rnorm = off;    off = align256(off + M * sizeof(float));
   L.partial = off;  off = align256(off + size_t(kMaxGrid) * M * sizeof(RowStat));
   const size_t zs_sample = size_t(B) * size_t(sample_slices(V)) * 2 * sizeof(double);
@@ -111,14 +125,15 @@ struct StatsArgs {
   float T, c;             // temperature and log2(e) / T
   int stats;              // write per-row partial statistics
   int want_q;             // also draft-logit statistics (softmax proposal, T > 0)
-  RowStat* partial;       // [gridDim][M]
+  RowStat* partial;       // [M][gridDim]
   float* rnorm;           // [M] RMSNorm factor of every row (written by workgroup 0), or null
 };
 
 enum FinalizeKind { kFinalizeVerify = 1, kFinalizeScore = 2 };
 
-// Combine the partials of a request, then the acceptance scan (verify) or the outcome
-// marginals (score).  One workgroup per request.
+// Finalize, in two launches: per-row tasks (combine the partials of a row; the exact
+// logit of a draft row at its draft token) over a grid of one-wave workgroups, then per
+// request the acceptance scan (verify) or the outcome marginals (score).
 struct FinalArgs {
   const void* W;
   const void* gamma;
@@ -133,8 +148,10 @@ struct FinalArgs {
   int mode;
   int kind;               // FinalizeKind
   uint64_t seed, offset;
-  int P;                  // partial records per row
-  const RowStat* partial;
+  int P;                  // partial records per row (LM-head workgroups)
+  const RowStat* partial; // [M][P]
+  RowStat* rowstat;       // [M] combined statistics
+  DraftLogit* dlog;       // [M] (rows < K of each request)
   const float* rnorm;
   int* n_accepted;
   int* committed;
@@ -155,8 +172,6 @@ struct SampleArgs {
   int mode;
   const float* logits;
   const float* G;
-  const int* drafts;
-  const RowFinal* rowfinal;
   const ReqState* req;
   double* zs;             // [B][slices][2]
   int* committed;

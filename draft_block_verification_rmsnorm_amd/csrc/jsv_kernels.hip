@@ -3,9 +3,10 @@
 //   stats_kernel     fused final RMSNorm + LM head (bf16 MFMA 16x16x32, or f32 MFMA
 //                    16x16x4) whose epilogue writes the logits and per-row online softmax
 //                    statistics of its vocabulary range (JetSpec++ paper §4.2 "Decoder").
-//   finalize_kernel  per request: combine the statistics, the exact logit at each draft
-//                    token, then the acceptance scan (paper §3, App. F.3) or the outcome
-//                    marginals (§4.2 Eq. 6).
+//   rowstat_kernel   per row: combine the partial statistics, and the exact logit at
+//                    each draft token (one wave per task, spread over the chip).
+//   scan_kernel      per request: the acceptance scan (paper §3, App. F.3) or the
+//                    outcome marginals (§4.2 Eq. 6).
 //   slice_sum_kernel / locate_kernel
 //                    bonus token by inverse CDF over the residual of the rejected row
 //                    (§3): residual mass per vocabulary slice, then the CDF step.
@@ -78,6 +79,85 @@ __device__ inline float bload4f(rsrc_t r, uint32_t voff) {
 }
 __device__ inline void bstore4f(float x, rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, 0, 0);
+}
+// Same, marked non-temporal (streaming data the writer does not read again).
+__device__ inline void bstore4f_nt(float x, rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, 0, 2);
+}
+
+__device__ inline double u2d(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | uint64_t(lo));
+}
+
+// ------------------------------------------------------------------------------------
+// Cross-lane moves on the DPP path (a VALU operand modifier, no LDS round trip), and
+// lane reads into scalar registers for wave-uniform lane indices.
+//   0xB1 / 0x4E   quad_perm [1,0,3,2] / [2,3,0,1]   (lane ^ 1, lane ^ 2)
+//   0x111..0x118  row_shr:1..8                     (within 16-lane rows)
+//   0x124, 0x128  row_ror:4, row_ror:8
+//   0x142, 0x143  row_bcast:15, row_bcast:31       (last lane of a row into later rows)
+// Lanes whose source is outside the pattern, or whose row is masked off, read zero.
+template <int CTRL, int ROWS = 0xf>
+__device__ inline uint32_t dpp32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, ROWS, 0xf, false));
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ inline float dppf(float x) {
+  return __uint_as_float(dpp32<CTRL, ROWS>(__float_as_uint(x)));
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ inline double dppd(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint64_t lo = dpp32<CTRL, ROWS>(uint32_t(u)), hi = dpp32<CTRL, ROWS>(uint32_t(u >> 32));
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+__device__ inline float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ inline int readlane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ inline double readlane_d(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint64_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u)), l));
+  const uint64_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(u >> 32)), l));
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts, then row broadcasts.
+__device__ inline double wave_incl_scan(double x) {
+  x += dppd<0x111>(x);
+  x += dppd<0x112>(x);
+  x += dppd<0x114>(x);
+  x += dppd<0x118>(x);
+  x += dppd<0x142, 0xa>(x);
+  x += dppd<0x143, 0xc>(x);
+  return x;
+}
+// Sum over the 64 lanes (the last lane of the inclusive scan), in every lane.
+__device__ inline double wave_sum(double x) { return readlane_d(wave_incl_scan(x), kWave - 1); }
+
+// Lane l receives the sum of lanes l mod 16 + 16 i, i = 0..3 (the four 16-lane rows, in
+// the order (r0 + r1) + (r2 + r3)), through gfx950's row-swapping permlanes.
+__device__ inline uint2 swap16(uint32_t x) {
+  const auto v = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return make_uint2(v[0], v[1]);
+}
+__device__ inline uint2 swap32(uint32_t x) {
+  const auto v = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return make_uint2(v[0], v[1]);
+}
+__device__ inline float rows_sum(float y) {
+  const uint2 a = swap16(__float_as_uint(y));
+  const float z = __uint_as_float(a.x) + __uint_as_float(a.y);
+  const uint2 b = swap32(__float_as_uint(z));
+  return __uint_as_float(b.x) + __uint_as_float(b.y);
+}
+__device__ inline double rows_sum(double y) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, y);
+  const uint2 lo = swap16(uint32_t(u)), hi = swap16(uint32_t(u >> 32));
+  const double z = u2d(lo.x, hi.x) + u2d(lo.y, hi.y);
+  const uint64_t w = __builtin_bit_cast(uint64_t, z);
+  const uint2 lo2 = swap32(uint32_t(w)), hi2 = swap32(uint32_t(w >> 32));
+  return u2d(lo2.x, hi2.x) + u2d(lo2.y, hi2.y);
 }
 
 // ------------------------------------------------------------------------------------
@@ -224,21 +304,57 @@ __device__ inline void stat_merge(Stat& a, const Stat& b, float c, bool soft) {
   a.flags |= b.flags;
 }
 
-__device__ inline Stat stat_shfl_xor(const Stat& a, int mask) {
+template <int CTRL>
+__device__ inline Stat stat_dpp(const Stat& a) {
   Stat o;
-  o.m = __shfl_xor(a.m, mask);
-  o.top2 = __shfl_xor(a.top2, mask);
-  o.mq = __shfl_xor(a.mq, mask);
-  o.idx = __shfl_xor(a.idx, mask);
-  o.s = __shfl_xor(a.s, mask);
-  o.sq = __shfl_xor(a.sq, mask);
-  o.flags = __shfl_xor(a.flags, mask);
+  o.m = dppf<CTRL>(a.m);
+  o.top2 = dppf<CTRL>(a.top2);
+  o.mq = dppf<CTRL>(a.mq);
+  o.idx = int(dpp32<CTRL>(uint32_t(a.idx)));
+  o.s = dppd<CTRL>(a.s);
+  o.sq = dppd<CTRL>(a.sq);
+  o.flags = dpp32<CTRL>(a.flags);
   return o;
+}
+
+__device__ inline Stat stat_readlane(const Stat& a, int l) {
+  Stat o;
+  o.m = readlane_f(a.m, l);
+  o.top2 = readlane_f(a.top2, l);
+  o.mq = readlane_f(a.mq, l);
+  o.idx = readlane_i(a.idx, l);
+  o.s = readlane_d(a.s, l);
+  o.sq = readlane_d(a.sq, l);
+  o.flags = uint32_t(readlane_i(int(a.flags), l));
+  return o;
+}
+
+// Merge over each 16-lane row; every lane of the row ends with the row's merge.  All
+// 16 sources are read in every step, so the result does not depend on what the other
+// lanes hold outside this row.
+__device__ inline void stat_row_reduce(Stat& st, float c, bool soft) {
+  stat_merge(st, stat_dpp<0xB1>(st), c, soft);
+  stat_merge(st, stat_dpp<0x4E>(st), c, soft);
+  stat_merge(st, stat_dpp<0x124>(st), c, soft);
+  stat_merge(st, stat_dpp<0x128>(st), c, soft);
+}
+
+// Merge over the whole wave, in every lane.
+__device__ inline void stat_wave_reduce(Stat& st, float c, bool soft) {
+  stat_row_reduce(st, c, soft);
+  Stat r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = stat_readlane(st, 16 * i);
+  st = r[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) stat_merge(st, r[i], c, soft);
 }
 
 __device__ inline Stat stat_load(const RowStat& r) {
   Stat s;
-  s.m = r.m; s.top2 = r.top2; s.mq = r.mq; s.idx = r.idx; s.s = r.s; s.sq = r.sq; s.flags = r.flags;
+  s.m = r.m; s.top2 = r.top2; s.mq = r.mq; s.s = r.s; s.sq = r.sq;
+  s.idx = int(r.idxf & kIdxMask);
+  s.flags = (r.idxf & kBadBit) ? uint32_t(JSV_FLAG_INVALID) : 0u;
   return s;
 }
 
@@ -260,6 +376,12 @@ constexpr int pick_window(int NT, int NKS) {
 }
 
 // ------------------------------------------------------------------------------------
+// Logit groups staged in LDS between write-outs (at most 96 KB of staging).
+constexpr int stage_groups(int NTOK) {
+  const int g = (96 * 1024) / (NTOK * 16 * 4);
+  return g > 64 ? 64 : g;
+}
+
 // Fused RMSNorm + LM head + statistics.  Workgroup wg owns 16-row vocabulary groups
 // [g0, g1); its 8 waves split d into equal k-slices.  Each wave keeps the normalised
 // hidden states of its slice for the NT full 16-token tiles in registers (MFMA B
@@ -267,8 +389,10 @@ constexpr int pick_window(int NT, int NKS) {
 // ahead, through a buffer resource over the workgroup's rows (rows past the vocabulary
 // read as zero).  NX further rows (at most one) are dotted on the VALU against their
 // normalised state in LDS.  Per group the 8 partial tiles are summed through LDS (in
-// fp64, fixed order) and thread (token jj, column ii) folds its logit into running
-// statistics; at the end the 16 threads of a token merge theirs into one partial.
+// fp64, fixed order); thread (token jj, column ii) folds its logit into running
+// statistics and parks it in LDS, and every SF groups the staged logits go out as whole
+// row runs (64-byte stores scattered between the W reads cost far more).  At the end
+// the 16 threads of a token merge their statistics into one partial.
 template <int DT, int NT, int NX, int NKS>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   constexpr int EPL = Elem<DT>::EPL, ESZ = Elem<DT>::ESZ, KS = 4 * EPL;
@@ -277,11 +401,14 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   constexpr int NEP = (NTOK + 31) / 32;     // tokens per epilogue thread
   constexpr int XLEN = kWaves * NKS * 4;    // 16-byte groups per hidden row
   constexpr int XPT = (XLEN + kThreads - 1) / kThreads;
+  constexpr int SF = stage_groups(NTOK);
   constexpr int NT1 = NT > 0 ? NT : 1, NX1 = NX > 0 ? NX : 1;
   static_assert(NTOK >= 1 && NTOK <= kRowsPerPass && NX <= 1, "tiling");
   __shared__ floatx4 red[2][kWaves][NT1][kWave];
   __shared__ float redx[2][kWaves][NX1][16];
   __shared__ uint4 xrow[NX1][XLEN];
+  __shared__ uint4 gsh[XLEN];
+  __shared__ float zst[NTOK][SF * 16];
   __shared__ double ssq[kWaves][kRowsPerPass];
   __shared__ float rnorm[kRowsPerPass];
 
@@ -304,48 +431,63 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     return bload16(wr, wvoff + uint32_t(s * KS * ESZ), uint32_t(g - g0) * 16u * rowbytes);
   };
 
-  // Start streaming W before the norm prologue.
-  uint4 fr[D];
-#pragma unroll
-  for (int j = 0; j < D; ++j) fr[j] = wload(g0, j);
-
   // ---- RMSNorm of the rows of this pass ----------------------------------------------
+  // The hidden-state and gamma loads are issued before the first W loads: a wave's
+  // loads return in issue order, so the norm does not wait behind W.
   const char* Hb = static_cast<const char*>(a.hidden) + (size_t)a.row0 * rowbytes;
-  const char* Gm = static_cast<const char*>(a.gamma);
   const rsrc_t hr = make_rsrc(Hb, (uint64_t)a.rows * rowbytes);
-  const rsrc_t gr = make_rsrc(Gm, rowbytes);
+  const rsrc_t gr = make_rsrc(a.gamma, rowbytes);
+  uint4 gq[XPT];
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int q = tid + j * kThreads;
+    gq[j] = bload16(gr, q < XLEN ? uint32_t(q) * 16u : kOutOfRange, 0);
+  }
   uint32_t tokoff[NT1];
 #pragma unroll
   for (int t = 0; t < NT1; ++t) {
     const int tok = t * 16 + (lane & 15);
     tokoff[t] = (t < NT && tok < a.rows) ? uint32_t(tok) * rowbytes : kOutOfRange;
   }
-  // Sums of squares of this wave's slice of every tile token (padding tokens read zeros).
+  uint4 xf[NT1][NKS];  // this wave's slice of the tile tokens (padding tokens read zeros)
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) xf[t][s] = bload16(hr, tokoff[t] + uint32_t(kb + s * KS) * ESZ, 0);
+  uint4 xh[NX1][XPT];  // the VALU row, block-wide
+#pragma unroll
+  for (int x = 0; x < NX; ++x)
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int q = tid + j * kThreads;
+      xh[x][j] = bload16(hr, (q < XLEN) ? uint32_t(NT * 16 + x) * rowbytes + uint32_t(q) * 16u
+                                        : kOutOfRange, 0);
+    }
+  asm volatile("" ::: "memory");  // keep the W loads behind the loads above
+  uint4 fr[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) fr[j] = wload(g0, j);
+
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int q = tid + j * kThreads;
+    if (q < XLEN) gsh[q] = gq[j];
+  }
+  // Sums of squares of this wave's slice of every token.
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     double ps = 0.0;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      ps += sumsq16<DT>(bload16(hr, tokoff[t] + uint32_t(kb + s * KS) * ESZ, 0));
-      if ((s & 3) == 3) asm volatile("" ::: "memory");  // bound the loads in flight here
-    }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    for (int s = 0; s < NKS; ++s) ps += sumsq16<DT>(xf[t][s]);
+    ps = rows_sum(ps);
     if (lane < 16) ssq[w][t * 16 + lane] = ps;
   }
-  // The VALU row: block-wide, XPT 16-byte groups per thread.
-  uint4 xh[NX1][XPT];
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
     double ps = 0.0;
 #pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int q = tid + j * kThreads;
-      const uint32_t off = (q < XLEN) ? uint32_t(NT * 16 + x) * rowbytes + uint32_t(q) * 16u : kOutOfRange;
-      xh[x][j] = bload16(hr, off, 0);
-      ps += sumsq16<DT>(xh[x][j]);
-    }
-    for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+    for (int j = 0; j < XPT; ++j) ps += sumsq16<DT>(xh[x][j]);
+    ps = wave_sum(ps);
     if (lane == 0) ssq[w][NT * 16 + x] = ps;
   }
   __syncthreads();
@@ -359,10 +501,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   }
   __syncthreads();
 
-  // Normalised hidden states of this wave's k-slice for the MFMA tiles (padding tokens
-  // get r = 0; their output columns are never used).  The rows are re-read (they are
-  // in cache by now) rather than held in registers across the reduction.
-  uint4 xf[NT1][NKS];
+  // Normalise in place (padding tokens get r = 0; their output columns are never used).
   {
     float rt[NT1];
 #pragma unroll
@@ -372,21 +511,18 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const uint4 g = bload16(gr, uint32_t(kb + s * KS) * ESZ, 0);
+      const uint4 g = gsh[(kb + s * KS) / EPL];
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        xf[t][s] = norm_pack<DT>(bload16(hr, tokoff[t] + uint32_t(kb + s * KS) * ESZ, 0), g, rt[t]);
-      if ((s & 3) == 3) asm volatile("" ::: "memory");  // bound the loads in flight here
+      for (int t = 0; t < NT; ++t) xf[t][s] = norm_pack<DT>(xf[t][s], g, rt[t]);
     }
   }
-  // The VALU row in LDS.
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
     const float r = rnorm[NT * 16 + x];
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int q = tid + j * kThreads;
-      if (q < XLEN) xrow[x][q] = norm_pack<DT>(xh[x][j], bload16(gr, uint32_t(q) * 16u, 0), r);
+      if (q < XLEN) xrow[x][q] = norm_pack<DT>(xh[x][j], gsh[q], r);
     }
   }
   if (NX > 0) __syncthreads();
@@ -402,14 +538,13 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   const rsrc_t qr = make_rsrc(a.G + (size_t)qrow0 * V, (uint64_t)qrows * (uint64_t)V * 4u);
   int jj[NEP];
   bool tok_ok[NEP], qrow[NEP];
-  uint32_t loff[NEP], qoff[NEP];
+  uint32_t qoff[NEP];
   Stat st[NEP];
 #pragma unroll
   for (int e = 0; e < NEP; ++e) {
     jj[e] = (tid >> 4) + 32 * e;
     tok_ok[e] = jj[e] < NTOK && jj[e] < a.rows;
     const int row = a.row0 + (tok_ok[e] ? jj[e] : 0);
-    loff[e] = uint32_t(row - a.row0) * uint32_t(V) * 4u;
     qrow[e] = false;
     qoff[e] = kOutOfRange;
     if (a.want_q && tok_ok[e]) {
@@ -420,6 +555,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   }
 
   int buf = 0;
+  int64_t gb = g0;  // first group of the staged run
   for (int64_t g = g0; g < g1; ++g) {
     const int64_t v = g * 16 + ii;
     const bool vok = v < V;
@@ -445,9 +581,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     }
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-      float y = xacc[x];
-      y += __shfl_xor(y, 16);
-      y += __shfl_xor(y, 32);
+      const float y = rows_sum(xacc[x]);
       if (lane < 16) redx[buf][w][x][lane] = y;
     }
 #pragma unroll
@@ -468,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       }
       const float z = float(zz);
       const bool valid = tok_ok[e] && vok;
-      bstore4f(z, lr, valid ? loff[e] + uint32_t(v) * 4u : kOutOfRange);
+      zst[jj[e]][int(g - gb) * 16 + ii] = z;
       if (a.stats) {
         Stat& S = st[e];
         const bool fin = fabsf(z) <= FLT_MAX;
@@ -484,121 +618,168 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
         }
       }
     }
+    if (g + 1 == g1 || int(g + 1 - gb) == SF) {  // write out the staged run
+      __syncthreads();
+      const int ncol = int(g + 1 - gb) * 16;
+      const uint32_t c0 = uint32_t(gb * 16);
+#pragma unroll
+      for (int rr = 0; rr < NTOK; ++rr) {
+        if (rr >= a.rows) break;
+        for (int cc = tid; cc < ncol; cc += kThreads) {
+          const uint32_t vv = c0 + uint32_t(cc);
+          bstore4f_nt(zst[rr][cc], lr, vv < uint32_t(V) ? uint32_t(rr) * uint32_t(V) * 4u + vv * 4u : kOutOfRange);
+        }
+      }
+      gb = g + 1;
+    }
     buf ^= 1;
   }
 
   if (!a.stats) return;
 #pragma unroll
   for (int e = 0; e < NEP; ++e) {
-    for (int off = 1; off < 16; off <<= 1) stat_merge(st[e], stat_shfl_xor(st[e], off), c, soft);
+    stat_row_reduce(st[e], c, soft);
     if (ii == 0 && tok_ok[e]) {
-      RowStat rs{};
+      RowStat rs;
       rs.s = st[e].s; rs.sq = st[e].sq; rs.m = st[e].m; rs.top2 = st[e].top2; rs.mq = st[e].mq;
-      rs.idx = st[e].idx; rs.flags = st[e].flags;
-      a.partial[(size_t)wg * a.M + a.row0 + jj[e]] = rs;
+      rs.idxf = (uint32_t(st[e].idx) & kIdxMask) | (st[e].flags ? kBadBit : 0u);
+      a.partial[(size_t)(a.row0 + jj[e]) * P + wg] = rs;
     }
   }
 }
 
 // ------------------------------------------------------------------------------------
-// Per-request finalize: grid B, kThreads threads.
-//   phase 0  exact (fp64) logit at each draft token, from the normalised row and W[d]
-//            (T > 0: alpha and 1 - alpha keep their digits when alpha is close to 1);
-//   phase A  combine every LM-head workgroup's partial statistics of the K+1 rows;
-//   phase B  wave 0, lane i = row i: acceptance probabilities, the scan to the first
-//            rejection with the Philox uniforms (verify) or the outcome marginals (score).
+// Finalize, part 1 (rowstat_kernel): grid (tasks, B) of one-wave workgroups, so that
+// the reads spread over the chip.  Task i < K (T > 0 only): the float64 logit of draft
+// row i at its draft token, from the normalised row and W[d_i], so that alpha and
+// 1 - alpha keep their digits when alpha is close to 1 (paper §3, acceptance rule).  The
+// other tasks merge the partial statistics of one row over every LM-head workgroup.
+// Part 2 (scan_kernel): grid B, one wave, lane i = row i: acceptance probabilities and
+// the scan to the first rejection with the Philox uniforms (verify: paper §3, App. F.3),
+// or the outcome marginals (score: §4.2 Eq. 6).
+
+// Float64 logit of hidden row `row` at vocabulary row `dt`, returned on every lane.  The
+// normalised row is rebuilt from h, gamma and the stored RMSNorm factor the way the
+// LM-head kernel builds it; all loads of a batch are in flight together.
 template <int DT>
-__device__ void exact_draft_logits(const FinalArgs& a, int b, double* zd_sh) {
-  constexpr int EPL = Elem<DT>::EPL, ESZ = Elem<DT>::ESZ;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int K = a.K, R = K + 1, d = a.d;
-  for (int i = w; i < K; i += kWaves) {
-    const int dt = a.drafts[b * K + i];
-    if (dt < 0 || (int64_t)dt >= a.V) continue;
-    const int row = b * R + i;
-    const float r = a.rnorm[row];
-    const char* hrow = static_cast<const char*>(a.hidden) + (size_t)row * d * ESZ;
-    const char* wrow = static_cast<const char*>(a.W) + (size_t)dt * d * ESZ;
-    const char* gm = static_cast<const char*>(a.gamma);
-    double acc = 0.0;
-    for (int k = lane * EPL; k < d; k += kWave * EPL) {
-      const uint4 xq = norm_pack<DT>(*reinterpret_cast<const uint4*>(hrow + (size_t)k * ESZ),
-                                     *reinterpret_cast<const uint4*>(gm + (size_t)k * ESZ), r);
-      float xv[EPL], wv[EPL];
-      unpack<DT>(xq, xv);
-      unpack<DT>(*reinterpret_cast<const uint4*>(wrow + (size_t)k * ESZ), wv);
+__device__ double exact_logit(const FinalArgs& a, int row, int dt, float r) {
+  constexpr int EPL = Elem<DT>::EPL;
+  constexpr int NJ = 8;  // 16-byte groups per lane and operand per batch
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t bytes = uint32_t(a.d) * uint32_t(Elem<DT>::ESZ);
+  const rsrc_t hr = make_rsrc(static_cast<const char*>(a.hidden) + (size_t)row * bytes, bytes);
+  const rsrc_t gr = make_rsrc(a.gamma, bytes);
+  const rsrc_t wr = make_rsrc(static_cast<const char*>(a.W) + (size_t)dt * bytes, bytes);
+  double acc = 0.0;
+  for (uint32_t base = 0; base < bytes; base += NJ * kWave * 16) {
+    uint4 hq[NJ], gq[NJ], wq[NJ];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc += double(xv[e]) * double(wv[e]);
+    for (int j = 0; j < NJ; ++j) {
+      const uint32_t off = base + uint32_t(j * kWave + lane) * 16u;
+      hq[j] = bload16(hr, off, 0);
+      gq[j] = bload16(gr, off, 0);
+      wq[j] = bload16(wr, off, 0);
     }
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) zd_sh[i] = acc;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float xv[EPL], wv[EPL];
+      unpack<DT>(norm_pack<DT>(hq[j], gq[j], r), xv);
+      unpack<DT>(wq[j], wv);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc = fma(double(xv[e]), double(wv[e]), acc);
+    }
+  }
+  return wave_sum(acc);
+}
+
+// Merge of the P partial records of one row, returned on every lane.
+__device__ Stat combine_row(const FinalArgs& a, int row, float c, bool soft) {
+  const int lane = threadIdx.x & (kWave - 1), P = a.P;
+  const rsrc_t pr = make_rsrc(a.partial + (size_t)row * P, uint64_t(P) * sizeof(RowStat));
+  Stat acc;
+  stat_init(acc);
+  for (int p0 = 0; p0 < P; p0 += 4 * kWave) {
+    uint4 lo[4], hi[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t off = uint32_t(p0 + j * kWave + lane) * uint32_t(sizeof(RowStat));
+      lo[j] = bload16(pr, off, 0);
+      hi[j] = bload16(pr, off + 16u, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Stat o;
+      stat_init(o);
+      if (p0 + j * kWave + lane < P) {
+        o.s = u2d(lo[j].x, lo[j].y);
+        o.sq = u2d(lo[j].z, lo[j].w);
+        o.m = __uint_as_float(hi[j].x);
+        o.top2 = __uint_as_float(hi[j].y);
+        o.mq = __uint_as_float(hi[j].z);
+        o.idx = int(hi[j].w & kIdxMask);
+        o.flags = (hi[j].w & kBadBit) ? uint32_t(JSV_FLAG_INVALID) : 0u;
+      }
+      stat_merge(acc, o, c, soft);
+    }
+  }
+  stat_wave_reduce(acc, c, soft);
+  return acc;
+}
+
+__global__ __launch_bounds__(kWave) void rowstat_kernel(FinalArgs a) {
+  const int t = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int K = a.K, R = K + 1;
+  const int64_t V = a.V;
+  const bool soft = a.T > 0.f;
+  const int nx = soft ? K : 0;
+  if (t < nx) {
+    const int row = b * R + t;
+    const int dt = a.drafts[b * K + t];
+    const float r = a.rnorm[row];
+    DraftLogit o{};
+    if (dt >= 0 && (int64_t)dt < V) {
+      if (a.mode == JSV_PROPOSAL_SOFTMAX) o.g = a.G[(size_t)(b * K + t) * V + dt];
+      o.z = (a.dtype == JSV_BF16) ? exact_logit<JSV_BF16>(a, row, dt, r)
+                                  : exact_logit<JSV_F32>(a, row, dt, r);
+    }
+    if (lane == 0) a.dlog[row] = o;
+  } else {
+    const float c = soft ? float(kLog2eD / double(a.T)) : 0.f;
+    const int row = b * R + (t - nx);
+    const Stat st = combine_row(a, row, c, soft);
+    if (lane == 0) {
+      RowStat rs;
+      rs.s = st.s; rs.sq = st.sq; rs.m = st.m; rs.top2 = st.top2; rs.mq = st.mq;
+      rs.idxf = (uint32_t(st.idx) & kIdxMask) | (st.flags ? kBadBit : 0u);
+      a.rowstat[row] = rs;
+    }
   }
 }
 
-__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
-  const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int K = a.K, R = K + 1, P = a.P;
+__global__ __launch_bounds__(kWave) void scan_kernel(FinalArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int K = a.K, R = K + 1;
   const int64_t V = a.V;
   const bool soft = a.T > 0.f;
-  const float c = soft ? float(kLog2eD / double(a.T)) : 0.f;
   const double cd = soft ? kLog2eD / double(a.T) : 0.0;
-  __shared__ Stat rows_sh[kMaxK + 1];
-  __shared__ double zd_sh[kMaxK];
-
-  if (soft) {
-    if (a.dtype == JSV_BF16) exact_draft_logits<JSV_BF16>(a, b, zd_sh);
-    else exact_draft_logits<JSV_F32>(a, b, zd_sh);
-  }
-  // Phase A: row i by wave i % kWaves, two rows per pass with their loads in flight.
-  const int M = a.B * R;
-  for (int i0 = w; i0 < R; i0 += 2 * kWaves) {
-    Stat acc[2];
-    stat_init(acc[0]);
-    stat_init(acc[1]);
-    for (int p0 = 0; p0 < P; p0 += 4 * kWave) {
-      RowStat ld[2][4];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = i0 + u * kWaves, p = p0 + j * kWave + lane;
-          if (i < R && p < P) {
-            ld[u][j] = a.partial[(size_t)p * M + b * R + i];
-          } else {
-            ld[u][j] = RowStat{};
-            ld[u][j].m = -INFINITY; ld[u][j].top2 = -INFINITY; ld[u][j].mq = -INFINITY;
-            ld[u][j].idx = INT_MAX;
-          }
-        }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) stat_merge(acc[u], stat_load(ld[u][j]), c, soft);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      for (int off = 32; off > 0; off >>= 1) stat_merge(acc[u], stat_shfl_xor(acc[u], off), c, soft);
-      const int i = i0 + u * kWaves;
-      if (lane == 0 && i < R) rows_sh[i] = acc[u];
-    }
-  }
-  __syncthreads();
-  if (w != 0) return;
-
-  // Phase B: lane i handles row i of request b.
+  const int di = (lane < K) ? a.drafts[b * K + lane] : -1;
+  DraftLogit dl{};
+  if (soft && lane < K) dl = a.dlog[b * R + lane];
+  // Lane i handles row i of request b.
   const bool act = lane <= K;
   const int row = b * R + lane;
   Stat st;
   stat_init(st);
-  if (act) st = rows_sh[lane];
-  const int di = (lane < K) ? a.drafts[b * K + lane] : -1;
+  if (act) st = stat_load(a.rowstat[row]);
   const bool bad = act && ((st.flags & JSV_FLAG_INVALID) || (lane < K && (di < 0 || (int64_t)di >= V)));
   if (__ballot(bad) != 0) {
     if (act && a.kind == kFinalizeVerify) a.committed[row] = -1;
     if (lane == 0) {
       if (a.kind == kFinalizeVerify) a.n_accepted[b] = -1;
       if (a.flags) a.flags[b] = JSV_FLAG_INVALID;
-      ReqState rq{}; rq.k = -1; rq.flags = JSV_FLAG_INVALID; a.req[b] = rq;
+      ReqState rq{};
+      rq.k = -1; rq.dk = -1; rq.flags = JSV_FLAG_INVALID;
+      a.req[b] = rq;
     }
     if (a.kind == kFinalizeScore) {
       if (lane < a.top_n) {
@@ -616,12 +797,11 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
     // Greedy verification: accept while the draft equals the row's argmax.
     alpha = (lane < K && di == st.idx) ? 1.0 : 0.0;
   } else if (lane < K) {
-    const double pd = exp2((zd_sh[lane] - double(st.m)) * cd) / st.s;
+    const double pd = exp2((dl.z - double(st.m)) * cd) / st.s;
     if (a.mode == JSV_PROPOSAL_POINT) {
       alpha = pd;
     } else {
-      const double gd = a.G[(size_t)(b * K + lane) * V + di];
-      const double qd = exp2((gd - double(st.mq)) * cd) / st.sq;
+      const double qd = exp2((double(dl.g) - double(st.mq)) * cd) / st.sq;
       alpha = (pd == 0.0) ? 0.0 : (pd >= qd ? 1.0 : pd / qd);
     }
   }
@@ -641,14 +821,14 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
     k = rej ? __builtin_ctzll(rej) : K;
     const bool tie = lane < K && lane <= k && fabs(u - alpha) < kAcceptTie;
     if (__ballot(tie)) f |= JSV_FLAG_ACCEPT_TIE;
-    vk = __shfl(v, k);
+    vk = readlane_d(v, k);
   }
-  const int bonus = __shfl(st.idx, k);
+  const int bonus = readlane_i(st.idx, k);
 
   // A_i = prod_{j<i} alpha_j (probability of reaching row i).
   double A = 1.0;
   for (int j = 0; j < K; ++j) {
-    const double aj = __shfl(alpha, j);
+    const double aj = readlane_d(alpha, j);
     if (j < lane) A *= aj;
   }
 
@@ -658,12 +838,20 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
     rf.m = st.m; rf.top2 = st.top2; rf.mq = st.mq; rf.idx = st.idx; rf.flags = st.flags;
     a.rowfinal[row] = rf;
   }
+  // Row k's statistics travel with the scan result: the bonus sampler reads nothing else.
+  ReqState rq{};
+  rq.vk = vk; rq.k = k; rq.flags = f;
+  rq.s = readlane_d(st.s, k); rq.sq = readlane_d(st.sq, k);
+  rq.m = readlane_f(st.m, k); rq.mq = readlane_f(st.mq, k);
+  const int dk = readlane_i(di, k);
+  rq.use_q = (a.mode == JSV_PROPOSAL_SOFTMAX && k < K) ? 1 : 0;
+  rq.dk = (a.mode == JSV_PROPOSAL_POINT && k < K) ? dk : -1;
   if (a.kind == kFinalizeVerify) {
     if (act) a.committed[row] = (lane < k) ? di : ((lane == k && !soft) ? bonus : -1);
     if (lane == 0) {
       a.n_accepted[b] = k;
       if (a.flags) a.flags[b] = f;
-      ReqState rq{}; rq.vk = vk; rq.k = k; rq.flags = f; a.req[b] = rq;
+      a.req[b] = rq;
     }
   } else {  // score
     if (act && a.len_marginal) {
@@ -676,7 +864,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
     }
     if (lane == 0) {
       if (a.flags) a.flags[b] = f;
-      ReqState rq{}; rq.k = k; rq.flags = f; a.req[b] = rq;
+      a.req[b] = rq;
     }
   }
 }
@@ -684,7 +872,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
 // ------------------------------------------------------------------------------------
 // Block-level helpers for the slice kernels (kSliceThreads = 256 = 4 waves).
 __device__ inline double block_sum(double x, double* sh) {
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  x = wave_sum(x);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
   if (lane == 0) sh[w] = x;
@@ -694,37 +882,6 @@ __device__ inline double block_sum(double x, double* sh) {
   __syncthreads();
   return t;
 }
-
-// Exclusive prefix sum over the block in thread order (deterministic).
-__device__ inline double block_exclusive_scan(double x, double* sh) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  double inc = x;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double y = __shfl_up(inc, off);
-    if (lane >= off) inc += y;
-  }
-  __syncthreads();
-  if (lane == kWave - 1) sh[w] = inc;
-  __syncthreads();
-  double base = 0.0;
-  for (int i = 0; i < w; ++i) base += sh[i];
-  __syncthreads();
-  return base + inc - x;
-}
-
-__device__ inline int block_min_int(int x, int* sh) {
-  for (int off = 32; off > 0; off >>= 1) x = min(x, __shfl_xor(x, off));
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) sh[w] = x;
-  __syncthreads();
-  int t = INT_MAX;
-  for (int i = 0; i < kSliceThreads / kWave; ++i) t = min(t, sh[i]);
-  __syncthreads();
-  return t;
-}
-
-__device__ inline int block_max_int(int x, int* sh) { return -block_min_int(-x, sh); }
 
 // Residual value r(v) and target probability p(v) of row k (paper §3; App. F.3).
 struct RowModel {
@@ -751,27 +908,48 @@ __device__ inline RowModel row_model(const RowFinal& rf, float c, int mode, int 
   return rm;
 }
 
+__device__ inline RowModel req_model(const ReqState& rq, float c) {
+  RowModel rm;
+  rm.m = rq.m; rm.mq = rq.mq; rm.c = c; rm.s = rq.s; rm.sq = rq.sq;
+  rm.use_q = rq.use_q != 0;
+  rm.dk = rq.dk;
+  return rm;
+}
+
 // ------------------------------------------------------------------------------------
-// Bonus sampler, part 1: grid (slices, B).  Residual mass (and target mass, for the
-// zero-residual fallback) of row k over each vocabulary slice.
+// Bonus sampler, part 1: grid (slices of kSampleSlice columns, B).  Residual mass (and
+// target mass, for the zero-residual fallback) of row k over each slice.
 __global__ __launch_bounds__(kSliceThreads) void slice_sum_kernel(SampleArgs a) {
-  const int b = blockIdx.y, j = blockIdx.x, NB = gridDim.x, tid = threadIdx.x;
+  const int b = blockIdx.y, j = blockIdx.x, tid = threadIdx.x, NB = gridDim.x;
   const ReqState rq = a.req[b];
   if (!(a.T > 0.f) || rq.k < 0) return;
   const int K = a.K, k = rq.k, row = b * (K + 1) + k;
-  const RowModel rm = row_model(a.rowfinal[row], a.c, a.mode, k, K, k < K ? a.drafts[b * K + k] : -1);
-  const int64_t V = a.V, L = (V + NB - 1) / NB, v0 = (int64_t)j * L;
-  const int n = (int)max<int64_t>(0, min<int64_t>(V, v0 + L) - v0);
-  const float* zr = a.logits + (size_t)row * V + v0;
-  const float* gr = rm.use_q ? a.G + (size_t)(b * K + k) * V + v0 : nullptr;
-  __shared__ double dsh[8];
-  double rs = 0.0, ps = 0.0;
-  for (int e = tid; e < n; e += kSliceThreads) {
-    double r, p;
-    rm.eval(v0 + e, zr[e], gr ? gr[e] : 0.f, r, p);
-    rs += r;
-    ps += p;
+  const RowModel rm = req_model(rq, a.c);
+  const int64_t V = a.V;
+  const uint32_t rowbytes = uint32_t(V) * 4u;
+  const rsrc_t zr = make_rsrc(a.logits + (size_t)row * V, rowbytes);
+  const rsrc_t gr = make_rsrc(rm.use_q ? a.G + (size_t)(b * K + k) * V : a.logits,
+                              rm.use_q ? rowbytes : 0u);
+  const int64_t v0 = (int64_t)j * kSampleSlice + tid;
+  float z[kSampleCols], g[kSampleCols];
+#pragma unroll
+  for (int e = 0; e < kSampleCols; ++e) {
+    const uint32_t off = uint32_t(v0 + e * kSliceThreads) * 4u;
+    z[e] = bload4f(zr, off);
+    g[e] = bload4f(gr, off);
   }
+  double rs = 0.0, ps = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSampleCols; ++e) {
+    const int64_t v = v0 + e * kSliceThreads;
+    if (v < V) {
+      double r, p;
+      rm.eval(v, z[e], g[e], r, p);
+      rs += r;
+      ps += p;
+    }
+  }
+  __shared__ double dsh[8];
   rs = block_sum(rs, dsh);
   ps = block_sum(ps, dsh);
   if (tid == 0) {
@@ -780,94 +958,112 @@ __global__ __launch_bounds__(kSliceThreads) void slice_sum_kernel(SampleArgs a) 
   }
 }
 
-// Bonus sampler, part 2: grid (B).  Locate t = v_k * Z among the slice totals, then walk
-// that slice with a block prefix sum to the first column whose CDF exceeds t.
-__global__ __launch_bounds__(kSliceThreads) void locate_kernel(SampleArgs a) {
-  const int b = blockIdx.x, tid = threadIdx.x, NB = sample_slices(a.V);
+// Bonus sampler, part 2: grid B, one wave.  t = v_k * Z is located among the slice
+// totals (rounds of 64 slices: a running base plus a wave prefix sum), then inside the
+// chosen slice (rounds of 64 consecutive columns): the token is the first column whose
+// CDF exceeds t.  Both passes over the slice totals form every sum in the same order,
+// so the CDF they walk ends exactly at the Z that t was taken from.
+constexpr int kLocRounds = 4;  // slice-total rounds kept in registers (V <= 262144)
+
+__global__ __launch_bounds__(kWave) void locate_kernel(SampleArgs a) {
+  constexpr int CR = kSampleSlice / kWave;  // column rounds inside a slice
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int NB = sample_slices(a.V), rounds = (NB + kWave - 1) / kWave;
+  const rsrc_t zsr = make_rsrc(a.zs + (size_t)b * NB * 2, uint64_t(NB) * 16u);
+  uint4 pre[kLocRounds];
+#pragma unroll
+  for (int q = 0; q < kLocRounds; ++q) pre[q] = bload16(zsr, uint32_t(q * kWave + lane) * 16u, 0);
+  auto totals = [&](int q) {
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kLocRounds; ++i)
+      if (q == i) x = pre[i];
+    if (q >= kLocRounds) x = bload16(zsr, uint32_t(q * kWave + lane) * 16u, 0);
+    return x;
+  };
   const ReqState rq = a.req[b];
   if (!(a.T > 0.f) || rq.k < 0) return;
   const int K = a.K, k = rq.k, row = b * (K + 1) + k;
-  const RowModel rm = row_model(a.rowfinal[row], a.c, a.mode, k, K, k < K ? a.drafts[b * K + k] : -1);
-  const int64_t V = a.V, L = (V + NB - 1) / NB;
-  __shared__ float zsh[kSampleMaxSlice];
-  __shared__ float gsh[kSampleMaxSlice];
-  __shared__ double dsh[8];
-  __shared__ int ish[8];
-  __shared__ double bc_base, bc_clo, bc_chi;
+  const RowModel rm = req_model(rq, a.c);
+  const int64_t V = a.V;
 
-  // slice totals: each thread owns a contiguous run of slices
-  const double* zsb = a.zs + (size_t)b * NB * 2;
-  const int SE = (NB + kSliceThreads - 1) / kSliceThreads;
-  const int q0 = tid * SE, q1 = min(NB, q0 + SE);
-  double xr = 0.0, xp = 0.0;
-  for (int q = q0; q < q1; ++q) { xr += zsb[2 * q]; xp += zsb[2 * q + 1]; }
-  const double Zr = block_sum(xr, dsh);
-  const double Zp = block_sum(xp, dsh);
-  const int zero = (Zr > 0.0) ? 0 : 1;
+  // pass 1: both totals
+  double Zr = 0.0, Zp = 0.0;
+  for (int q = 0; q < rounds; ++q) {
+    const uint4 x = totals(q);
+    Zr += wave_sum(u2d(x.x, x.y));
+    Zp += wave_sum(u2d(x.z, x.w));
+  }
+  const int zero = (Zr > 0.0) ? 0 : 1;  // no residual mass: draw from p_k (flagged)
   const double Z = zero ? Zp : Zr;
   const double t = rq.vk * Z;
-  double cb = block_exclusive_scan(zero ? xp : xr, dsh);
-  const double cb0 = cb;
-  int cand = INT_MAX, lastnz = -1;
-  double cbase = 0.0;
-  for (int q = q0; q < q1; ++q) {
-    const double x = zsb[2 * q + zero];
-    if (x > 0.0) lastnz = q;
-    if (cand == INT_MAX && x > 0.0 && cb + x > t) { cand = q; cbase = cb; }
-    cb += x;
-  }
-  const int sfound = block_min_int(cand, ish);
-  const int slast = block_max_int(lastnz, ish);
-  const int fall = (sfound == INT_MAX) ? 1 : 0;   // rounding left t at or above the last CDF value
-  const int s = fall ? (slast >= 0 ? slast : 0) : sfound;
-  if (!fall && cand == sfound) bc_base = cbase;
-  if (fall && q0 <= s && s < q1) {
-    double c2 = cb0;
-    for (int q = q0; q < s; ++q) c2 += zsb[2 * q + zero];
-    bc_base = c2;
-  }
-  // stage slice s
-  const int64_t v0 = (int64_t)s * L;
-  const int n = (int)max<int64_t>(0, min<int64_t>(V, v0 + L) - v0);
-  const float* zr = a.logits + (size_t)row * V;
-  const float* gr = rm.use_q ? a.G + (size_t)(b * K + k) * V : nullptr;
-  for (int e = tid; e < n; e += kSliceThreads) {
-    zsh[e] = zr[v0 + e];
-    if (gr) gsh[e] = gr[v0 + e];
-  }
-  __syncthreads();
-  const int E = (n + kSliceThreads - 1) / kSliceThreads;
-  const int e0 = tid * E, e1 = min(n, e0 + E);
-  double mine = 0.0;
-  for (int e = e0; e < e1; ++e) {
-    double r, p;
-    rm.eval(v0 + e, zsh[e], gr ? gsh[e] : 0.f, r, p);
-    mine += zero ? p : r;
-  }
-  double C = bc_base + block_exclusive_scan(mine, dsh);
-  int found = INT_MAX, last_pos = -1;
-  double clo = 0.0, chi = 0.0;
-  for (int e = e0; e < e1; ++e) {
-    double r, p;
-    rm.eval(v0 + e, zsh[e], gr ? gsh[e] : 0.f, r, p);
-    const double x = zero ? p : r;
-    const double Cn = C + x;
-    if (x > 0.0) last_pos = int(v0 + e);
-    if (found == INT_MAX && x > 0.0 && Cn > t) { found = int(v0 + e); clo = C; chi = Cn; }
-    C = Cn;
-  }
-  int tok = block_min_int(found, ish);
-  if (tok != INT_MAX && found == tok) { bc_clo = clo; bc_chi = chi; }
-  const int lastp = block_max_int(last_pos, ish);
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t f = zero ? JSV_FLAG_ZERO_RESIDUAL : 0u;
-    if (tok == INT_MAX || fall) {
-      tok = lastp;
-      f |= JSV_FLAG_CDF_TIE;
-    } else if ((t - bc_clo) < kCdfTie * Z || (bc_chi - t) < kCdfTie * Z) {
-      f |= JSV_FLAG_CDF_TIE;
+
+  // pass 2: the slice whose CDF step holds t
+  double base = 0.0, sbase = 0.0, slast_base = 0.0;
+  int s = -1, slast = -1;
+  for (int q = 0; q < rounds && s < 0; ++q) {
+    const uint4 x4 = totals(q);
+    const double x = zero ? u2d(x4.z, x4.w) : u2d(x4.x, x4.y);
+    const double inc = wave_incl_scan(x);
+    const double hi = base + inc, lo = hi - x;
+    const uint64_t hit = __ballot(x > 0.0 && hi > t);
+    const uint64_t pos = __ballot(x > 0.0);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      s = q * kWave + l;
+      sbase = readlane_d(lo, l);
+    } else if (pos) {
+      const int l = 63 - __builtin_clzll(pos);
+      slast = q * kWave + l;
+      slast_base = readlane_d(lo, l);
     }
+    base += readlane_d(inc, kWave - 1);
+  }
+  bool fall = s < 0;  // rounding left t at or above the last step: take the last mass
+  if (fall) { s = slast; sbase = slast_base; }
+
+  // inside slice s: round e covers columns c0 + 64 e + lane
+  const uint32_t rowbytes = uint32_t(V) * 4u;
+  const rsrc_t zr = make_rsrc(a.logits + (size_t)row * V, rowbytes);
+  const rsrc_t gr = make_rsrc(rm.use_q ? a.G + (size_t)(b * K + k) * V : a.logits,
+                              rm.use_q ? rowbytes : 0u);
+  const int64_t c0 = (int64_t)s * kSampleSlice;
+  float z[CR], g[CR];
+#pragma unroll
+  for (int e = 0; e < CR; ++e) {
+    const uint32_t off = uint32_t(c0 + e * kWave + lane) * 4u;
+    z[e] = bload4f(zr, off);
+    g[e] = bload4f(gr, off);
+  }
+  int tok = -1, lastpos = -1;
+  double C = sbase, clo = 0.0, chi = 0.0;
+#pragma unroll
+  for (int e = 0; e < CR; ++e) {
+    const int64_t v = c0 + e * kWave + lane;
+    double r = 0.0, p = 0.0;
+    if (v >= 0 && v < V) rm.eval(v, z[e], g[e], r, p);
+    const double x = zero ? p : r;
+    const double inc = wave_incl_scan(x);
+    const double hi = C + inc;
+    const uint64_t hit = (tok < 0 && !fall) ? __ballot(x > 0.0 && hi > t) : 0ull;
+    const uint64_t pos = __ballot(x > 0.0);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      tok = int(c0 + e * kWave + l);
+      chi = readlane_d(hi, l);
+      clo = chi - readlane_d(x, l);
+    }
+    if (pos) lastpos = int(c0 + e * kWave + 63 - __builtin_clzll(pos));
+    C += readlane_d(inc, kWave - 1);
+  }
+  uint32_t f = zero ? uint32_t(JSV_FLAG_ZERO_RESIDUAL) : 0u;
+  if (tok >= 0) {
+    if ((t - clo) < kCdfTie * Z || (chi - t) < kCdfTie * Z) f |= JSV_FLAG_CDF_TIE;
+  } else {
+    tok = lastpos;
+    f |= JSV_FLAG_CDF_TIE;
+  }
+  if (lane == 0) {
     a.committed[row] = tok;
     if (a.flags) a.flags[b] |= f;
   }
@@ -886,12 +1082,27 @@ __device__ inline bool key_better(const Key& x, const Key& y) {
   return x.v < y.v;
 }
 
+template <int CTRL>
+__device__ inline void key_dpp_max(Key& k) {
+  Key o;
+  o.r = dppd<CTRL>(k.r); o.p = dppd<CTRL>(k.p); o.v = int(dpp32<CTRL>(uint32_t(k.v)));
+  if (key_better(o, k)) k = o;
+}
+
 __device__ inline Key block_best(Key k, Key* sh) {
-  for (int off = 32; off > 0; off >>= 1) {
-    Key o;
-    o.r = __shfl_xor(k.r, off); o.p = __shfl_xor(k.p, off); o.v = __shfl_xor(k.v, off);
-    if (key_better(o, k)) k = o;
+  key_dpp_max<0xB1>(k);
+  key_dpp_max<0x4E>(k);
+  key_dpp_max<0x124>(k);
+  key_dpp_max<0x128>(k);
+  Key r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // the four row winners, in every lane
+    r[i].r = readlane_d(k.r, 16 * i); r[i].p = readlane_d(k.p, 16 * i); r[i].v = readlane_i(k.v, 16 * i);
   }
+  k = r[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (key_better(r[i], k)) k = r[i];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
   if (lane == 0) sh[w] = k;
@@ -981,7 +1192,7 @@ __global__ __launch_bounds__(kSliceThreads) void score_merge_kernel(ScoreArgs a)
     for (int kk = w; kk < R; kk += kSliceThreads / kWave) {
       double x = 0.0;
       for (int q = lane; q < NB; q += kWave) x += a.zs[((size_t)(b * R + kk)) * NB + q];
-      for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+      x = wave_sum(x);
       if (lane == 0) zk_sh[kk] = x;
     }
   }
@@ -1084,7 +1295,11 @@ hipError_t launch_stats(int dtype, int nks, int grid, const StatsArgs& a, hipStr
 }
 
 hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(a.B), dim3(kThreads), 0, stream, a);
+  const int tasks = (a.T > 0.f ? a.K : 0) + a.K + 1;
+  hipLaunchKernelGGL(rowstat_kernel, dim3(tasks, a.B), dim3(kWave), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_kernel, dim3(a.B), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1093,7 +1308,7 @@ hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(locate_kernel, dim3(a.B), dim3(kSliceThreads), 0, stream, a);
+  hipLaunchKernelGGL(locate_kernel, dim3(a.B), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
