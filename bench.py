@@ -7,10 +7,17 @@ resident in HBM before the timed region.  Prints one JSON line.
 
   python bench.py [--steps 50] [--warmup 5] [--config qwen8b_k16] [--no-cpu-baseline]
   python bench.py --copy-probe     # plain device copy of known size (counter calibration)
+  python bench.py --pmc-summary DIR
+      turn four rocprofv3 counter runs under DIR (bench_FETCH_SIZE, bench_WRITE_SIZE,
+      copy_FETCH_SIZE, copy_WRITE_SIZE, each holding run_counter_collection.csv) into
+      profiles/stats_kernel_<config>_traffic.{json,md}; the bench line reports that
+      traffic only while the kernel sources still hash to what was measured.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -19,6 +26,10 @@ from pathlib import Path
 
 ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
+KERNEL_SOURCES = ("draft_block_verification_rmsnorm_amd/csrc/jsv_kernels.hip",
+                  "draft_block_verification_rmsnorm_amd/csrc/jsv_internal.h",
+                  "draft_block_verification_rmsnorm_amd/csrc/jsv_api.hip")
+COPY_PROBE_BYTES = 1 << 30
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0
@@ -35,6 +46,64 @@ def algorithmic_bytes(cfg, T, mode_softmax):
     return b
 
 
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()
+
+
+def traffic_path(config):
+    return ROOT / "profiles" / f"stats_kernel_{config}_traffic.json"
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the LM-head kernel from the committed counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    p = traffic_path(config)
+    if not p.exists():
+        return None
+    t = json.loads(p.read_text())
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t["traffic_bytes_per_launch"]
+
+
+def _counter_means(csv_path, name_prefix):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Kernel_Name"].startswith(name_prefix)]
+    if not vals:
+        raise SystemExit(f"no dispatch of {name_prefix!r} in {csv_path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(pmc_dir, config):
+    """Counter runs -> traffic summary.  FETCH_SIZE and WRITE_SIZE are KiB per dispatch;
+    each is scaled by the factor that makes the 1 GiB copy read and write 1 GiB."""
+    d = Path(pmc_dir)
+    kname = "void jsv::stats_kernel"
+    f_kib, nf = _counter_means(d / "bench_FETCH_SIZE" / "run_counter_collection.csv", kname)
+    w_kib, nw = _counter_means(d / "bench_WRITE_SIZE" / "run_counter_collection.csv", kname)
+    cf_kib, _ = _counter_means(d / "copy_FETCH_SIZE" / "run_counter_collection.csv", "__amd_rocclr_copyBuffer")
+    cw_kib, _ = _counter_means(d / "copy_WRITE_SIZE" / "run_counter_collection.csv", "__amd_rocclr_copyBuffer")
+    sf = COPY_PROBE_BYTES / (cf_kib * 1024.0)
+    sw = COPY_PROBE_BYTES / (cw_kib * 1024.0)
+    fetch = f_kib * 1024.0 * sf
+    write = w_kib * 1024.0 * sw
+    import synth
+    cfg = synth.CONFIGS[config]
+    abytes = algorithmic_bytes(cfg, 1.0, True)
+    out = {"kernel": kname, "config": config, "kernel_source_sha256": kernel_source_hash(),
+           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+           "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib, "copy_bytes": COPY_PROBE_BYTES,
+           "fetch_scale": sf, "write_scale": sw,
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "traffic_bytes_per_launch": fetch + write, "algorithmic_bytes": abytes}
+    traffic_path(config).parent.mkdir(exist_ok=True)
+    traffic_path(config).write_text(json.dumps(out, indent=1) + "\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -45,7 +114,10 @@ def main():
     ap.add_argument("--point", action="store_true", help="point-mass proposal instead of softmax")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pmc-summary", metavar="DIR")
     args = ap.parse_args()
+    if args.pmc_summary:
+        return pmc_summary(args.pmc_summary, args.config)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -132,7 +204,8 @@ def main():
                        "call_p90": round(call[int(0.9 * (len(call) - 1))], 4),
                        "stats_kernel_mean": round(k1_ms, 4), "accept_and_bonus_mean": round(mean(k2), 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(args.config) if (T > 0 and not args.point) else None,
                      "kernel": "stats_kernel (fused RMSNorm + LM head + softmax statistics)",
                      "algorithmic_bytes": abytes},
         "accepted_last_step": n_acc,
@@ -144,7 +217,8 @@ def main():
 
 def cpu_baseline(cfg, head_cpu, blk, T, mode):
     """The oracle as it stands, on the host cores, over a bounded sample of the same
-    workload: whole verification calls on the same block, until ~10 s have passed."""
+    workload: whole verification calls on the same block, at least 3 and until ~12 s of
+    CPU work have passed."""
     import numpy as np
     import oracle
     try:
@@ -156,7 +230,7 @@ def cpu_baseline(cfg, head_cpu, blk, T, mode):
     dl = blk.draft_logits if mode == oracle.PROPOSAL_SOFTMAX else None
     times = []
     t_start = time.perf_counter()
-    while not times or (time.perf_counter() - t_start < 10.0 and len(times) < 5):
+    while len(times) < 3 or (time.perf_counter() - t_start < 12.0 and len(times) < 50):
         t0 = time.perf_counter()
         oracle.verify_block(oh, blk.hidden, blk.draft_tokens.numpy(), dl, T, mode, 1234, len(times))
         times.append(time.perf_counter() - t0)
@@ -170,7 +244,7 @@ def cpu_baseline(cfg, head_cpu, blk, T, mode):
 def copy_probe(torch):
     """A plain device-to-device copy of 1 GiB, five times: the bytes are known exactly, so
     its FETCH_SIZE / WRITE_SIZE counters calibrate the counters of the verification kernels."""
-    n = 1 << 30
+    n = COPY_PROBE_BYTES
     a = torch.ones(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     torch.cuda.synchronize()

@@ -31,7 +31,7 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr double kAcceptTie = 1e-4;
 constexpr float kLogitGapTie = 1e-3f;
-constexpr double kCdfTie = 1e-8;
+constexpr double kCdfTie = 1e-8;  // absolute, in probability mass (C and t are unnormalised)
 constexpr double kTopNTie = 1e-3;
 constexpr double kLog2eD = 1.4426950408889634074;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every resource used here
@@ -1058,7 +1058,7 @@ __global__ __launch_bounds__(kWave) void locate_kernel(SampleArgs a) {
   }
   uint32_t f = zero ? uint32_t(JSV_FLAG_ZERO_RESIDUAL) : 0u;
   if (tok >= 0) {
-    if ((t - clo) < kCdfTie * Z || (chi - t) < kCdfTie * Z) f |= JSV_FLAG_CDF_TIE;
+    if ((t - clo) < kCdfTie || (chi - t) < kCdfTie) f |= JSV_FLAG_CDF_TIE;
   } else {
     tok = lastpos;
     f |= JSV_FLAG_CDF_TIE;

@@ -67,7 +67,8 @@ typedef enum {
 /* Per-request flag bits written to `flags`. */
 #define JSV_FLAG_ACCEPT_TIE    (1u << 0) /* T > 0: |u_i - alpha_i| < 1e-4 at a row the scan reached   */
 #define JSV_FLAG_LOGIT_GAP     (1u << 1) /* T = 0: top-2 logit gap < 1e-3 at a row that decided k or a */
-#define JSV_FLAG_CDF_TIE       (1u << 2) /* bonus target within 1e-8 * Z of a CDF step, or fell through */
+#define JSV_FLAG_CDF_TIE       (1u << 2) /* bonus target within 1e-8 (probability mass) of a CDF step,
+                                            or rounding left it past the last step          */
 #define JSV_FLAG_INVALID       (1u << 3) /* non-finite logits or a draft token outside [0, vocab)       */
 #define JSV_FLAG_ZERO_RESIDUAL (1u << 4) /* residual mass 0 at the rejected row: sampled p_k instead    */
 #define JSV_FLAG_TOPN_TIE      (1u << 5) /* adjacent outcomes among the top N+1 within 1e-3 relative    */

@@ -36,13 +36,16 @@ from .philox import block_uniforms_np
 # ---- per-request flag bits (the C header documents the same bits) -------------
 FLAG_ACCEPT_TIE = 1 << 0      # |u_i - alpha_i| < ACCEPT_TIE at a row the scan reached (T > 0)
 FLAG_LOGIT_GAP = 1 << 1       # top-2 logit gap < LOGIT_GAP_TIE at a deciding row (T = 0)
-FLAG_CDF_TIE = 1 << 2         # sampling target within CDF_TIE * Z of a CDF step, or fell through
+FLAG_CDF_TIE = 1 << 2         # sampling target within CDF_TIE (probability mass) of a CDF step, or fell through
 FLAG_INVALID = 1 << 3         # non-finite logits or a draft token outside [0, V)
 FLAG_ZERO_RESIDUAL = 1 << 4   # residual mass Z = 0: sampled the target row instead
 FLAG_TOPN_TIE = 1 << 5        # adjacent top-(N+1) outcome probabilities within TOPN_TIE (relative)
 
 ACCEPT_TIE = 1e-4
 LOGIT_GAP_TIE = 1e-3
+# The CDF window is absolute, in units of probability mass: an error dz in the logits
+# moves C(a) by at most sum_w p(w) |dz_w| / T whatever the residual mass Z is, so a window
+# relative to Z would shrink exactly where the residual is small and the draw sensitive.
 CDF_TIE = 1e-8
 TOPN_TIE = 1e-3
 
@@ -166,8 +169,8 @@ def inverse_cdf(r, v):
 
     C(a) = r_0 + ... + r_a summed left to right in float64; Z = C(V-1); t = v * Z;
     the token is the first a with C(a) > t.  Returns (token, flags): FLAG_CDF_TIE if t
-    lies within CDF_TIE * Z of either end of the chosen step, or if rounding left no
-    such a (then the last token with r > 0 is taken).
+    lies within CDF_TIE of either end of the chosen step, or if rounding left no such a
+    (then the last token with r > 0 is taken).
     """
     C = np.cumsum(np.asarray(r, dtype=np.float64))
     Z = float(C[-1])
@@ -179,7 +182,7 @@ def inverse_cdf(r, v):
         flags |= FLAG_CDF_TIE
     lo = float(C[a - 1]) if a > 0 else 0.0
     hi = float(C[a])
-    if (t - lo) < CDF_TIE * Z or (hi - t) < CDF_TIE * Z:
+    if (t - lo) < CDF_TIE or (hi - t) < CDF_TIE:
         flags |= FLAG_CDF_TIE
     return a, flags
 

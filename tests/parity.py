@@ -3,7 +3,7 @@ seeded inputs and compare them to the bar the method fixes.
 
   * accepted length, committed tokens and top-N (length, token) pairs: bit-exact,
     except for requests either side flags as a near-tie (|u - alpha| < 1e-4, top-2
-    logit gap < 1e-3, the sampling target within 1e-8 Z of a CDF step, or adjacent
+    logit gap < 1e-3, the sampling target within 1e-8 of a CDF step, or adjacent
     top-(N+1) probabilities within 1e-3); those are counted and checked for validity;
   * logits: |GPU - oracle| <= 2e-2 absolute;
   * probabilities (outcome probabilities, length marginals): 1e-3 relative where the

@@ -105,6 +105,45 @@ def test_verify_qwen8b_k16(qwen, dev, T, mode):
     assert st["exact"] >= 2
 
 
+def _cdf_drift(zg, zo, g, T):
+    """How far the logit error can move a bonus decision: the largest difference of the
+    residual CDFs built from two logit rows (same draft logits g, or the target row alone
+    when g is None), plus the move of the total Z (t = v Z moves by at most that), in
+    float64 and in units of probability mass."""
+    def resid(z):
+        p = np.exp((z - z.max()) / T)
+        p /= p.sum()
+        if g is None:
+            return p
+        q = np.exp((g - g.max()) / T)
+        q /= q.sum()
+        return np.maximum(p - q, 0.0)
+    cg, co = np.cumsum(resid(np.asarray(zg, np.float64))), np.cumsum(resid(np.asarray(zo, np.float64)))
+    return float(np.max(np.abs(cg - co)) + abs(cg[-1] - co[-1]))
+
+
+def test_cdf_drift_within_window(qwen, dev):
+    """The kernel's fp32-accumulated logits move the residual CDF by less than half the CDF
+    near-tie window at the Qwen3-8B shape, on every row of several blocks (K = 16 and the
+    K = 32 generator), so a bonus draw that the logit error could flip is always flagged."""
+    T = 1.0
+    worst = 0.0
+    for name, seeds in (("qwen8b_k16", 3), ("qwen8b_k32_b4", 2)):
+        cfg = synth.CONFIGS[name]
+        ws = jsv.new_workspace(qwen.gpu, 1, cfg.K)
+        for seed in range(seeds):
+            say(f"{name} CDF drift seed={seed}")
+            blk = synth.make_block(qwen.cpu, 1, cfg.K, cfg.sigma, T, seed=100 + seed)
+            got, ref = run_verify(qwen, blk, T, SOFT, seed, 0, ws)
+            zo = ref["logits"][0]
+            G = blk.draft_logits[0].numpy().astype(np.float64)
+            for i in range(cfg.K + 1):
+                dr = _cdf_drift(got["logits"][0, i], zo[i], G[i] if i < cfg.K else None, T)
+                worst = max(worst, dr)
+    say(f"  largest CDF drift {worst:.3e} (window {oracle.CDF_TIE:.0e})")
+    assert worst < 0.5 * oracle.CDF_TIE
+
+
 def test_verify_qwen8b_k32_b4(qwen, dev):
     cfg = synth.CONFIGS["qwen8b_k32_b4"]
     ws = jsv.new_workspace(qwen.gpu, cfg.batch, cfg.K)

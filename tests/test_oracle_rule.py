@@ -240,6 +240,15 @@ def test_inverse_cdf_steps():
     assert tok == 1 and flags == 0
 
 
+def test_inverse_cdf_window_is_absolute():
+    # a small residual mass (Z = 1e-3): the window stays 1e-8 of probability mass
+    r = np.array([0.1, 0.0, 0.3, 0.6]) * 1e-3
+    tok, flags = oracle.inverse_cdf(r, (1e-4 + 5e-9) / 1e-3)
+    assert tok == 2 and flags & oracle.FLAG_CDF_TIE
+    tok, flags = oracle.inverse_cdf(r, (1e-4 + 5e-8) / 1e-3)
+    assert tok == 2 and not flags & oracle.FLAG_CDF_TIE
+
+
 def test_committed_count_includes_bonus():
     # tau convention (paper §3, §5.1): a round commits the accepted prefix plus one bonus token
     rng = np.random.default_rng(8)
