@@ -26,6 +26,7 @@ namespace jsv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -164,11 +165,10 @@ __device__ inline double rows_sum(double y) {
 // Element helpers.
 __device__ inline float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
-__device__ inline uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  const floatx2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 template <int DT> struct Elem;
@@ -225,7 +225,7 @@ __device__ inline uint4 norm_pack(const uint4& hq, const uint4& gq, float r) {
   if constexpr (DT == JSV_BF16) {
     uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = f32_to_bf16_rne(y[2 * e]) | (f32_to_bf16_rne(y[2 * e + 1]) << 16);
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
     return make_uint4(w[0], w[1], w[2], w[3]);
   } else {
     return make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
@@ -376,14 +376,17 @@ constexpr int pick_window(int NT, int NKS) {
 }
 
 // ------------------------------------------------------------------------------------
+template <bool B> struct Tag { static constexpr bool value = B; };
+
 // Logit groups staged in LDS between write-outs (at most 96 KB of staging).
 constexpr int stage_groups(int NTOK) {
   const int g = (96 * 1024) / (NTOK * 16 * 4);
   return g > 64 ? 64 : g;
 }
 
-// Fused RMSNorm + LM head + statistics.  Workgroup wg owns 16-row vocabulary groups
-// [g0, g1); its 8 waves split d into equal k-slices.  Each wave keeps the normalised
+// Fused RMSNorm + LM head + statistics.  Workgroup wg owns the vocabulary rows [r0, r1),
+// an equal share taken 16 rows (one group) at a time; its 8 waves split d into equal
+// k-slices.  Each wave keeps the normalised
 // hidden states of its slice for the NT full 16-token tiles in registers (MFMA B
 // operand) and streams the same slice of W straight into MFMA A operands, D k-steps
 // ahead, through a buffer resource over the workgroup's rows (rows past the vocabulary
@@ -416,19 +419,17 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   const int P = gridDim.x, wg = blockIdx.x;
   const int64_t V = a.V;
   const int d = a.d;
-  const int64_t ngroups = (V + 15) >> 4;
-  const int64_t g0 = ngroups * wg / P, g1 = ngroups * (wg + 1) / P;
+  const int64_t r0 = V * wg / P, r1 = V * (wg + 1) / P;  // this workgroup's vocabulary rows
+  const int ng = int((r1 - r0 + 15) >> 4);                // 16-row groups, the last may be partial
   const int kb = w * (NKS * KS) + (lane >> 4) * EPL;
   const uint32_t rowbytes = uint32_t(d) * ESZ;
 
-  // W rows [16*g0, min(V, 16*g1)) as one buffer; group g of it at soffset (g-g0)*16 rows.
-  const int64_t wrow0 = g0 * 16;
-  const int64_t wrows = (V < g1 * 16 ? V : g1 * 16) - wrow0;
-  const rsrc_t wr = make_rsrc(static_cast<const char*>(a.W) + (size_t)wrow0 * rowbytes,
-                              (uint64_t)(wrows > 0 ? wrows : 0) * rowbytes);
+  // W rows [r0, r1) as one buffer; local group g of it at soffset 16 g rows.
+  const rsrc_t wr = make_rsrc(static_cast<const char*>(a.W) + (size_t)r0 * rowbytes,
+                              (uint64_t)(r1 - r0) * rowbytes);
   const uint32_t wvoff = uint32_t(lane & 15) * rowbytes + uint32_t(kb) * ESZ;
-  auto wload = [&](int64_t g, int s) -> uint4 {
-    return bload16(wr, wvoff + uint32_t(s * KS * ESZ), uint32_t(g - g0) * 16u * rowbytes);
+  auto wload = [&](int g, int s) -> uint4 {
+    return bload16(wr, wvoff + uint32_t(s * KS * ESZ), uint32_t(g) * 16u * rowbytes);
   };
 
   // ---- RMSNorm of the rows of this pass ----------------------------------------------
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   asm volatile("" ::: "memory");  // keep the W loads behind the loads above
   uint4 fr[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) fr[j] = wload(g0, j);
+  for (int j = 0; j < D; ++j) fr[j] = wload(0, j);
 
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
@@ -501,20 +502,14 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   }
   __syncthreads();
 
-  // Normalise in place (padding tokens get r = 0; their output columns are never used).
-  {
-    float rt[NT1];
+  // The tile tokens are normalised in place step by step inside the first group, where
+  // the VALU work overlaps the W stream (padding tokens get r = 0; their output columns
+  // are never used).  The VALU row is normalised into LDS here.
+  float rt[NT1];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int tok = t * 16 + (lane & 15);
-      rt[t] = tok < a.rows ? rnorm[tok] : 0.f;
-    }
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      const uint4 g = gsh[(kb + s * KS) / EPL];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) xf[t][s] = norm_pack<DT>(xf[t][s], g, rt[t]);
-    }
+  for (int t = 0; t < NT1; ++t) {
+    const int tok = t * 16 + (lane & 15);
+    rt[t] = (t < NT && tok < a.rows) ? rnorm[tok] : 0.f;
   }
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
@@ -555,10 +550,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   }
 
   int buf = 0;
-  int64_t gb = g0;  // first group of the staged run
-  for (int64_t g = g0; g < g1; ++g) {
-    const int64_t v = g * 16 + ii;
-    const bool vok = v < V;
+  int gb = 0;  // first group of the staged run
+  auto group = [&](int g, auto first) {
+    constexpr bool FIRST = decltype(first)::value;
+    const int64_t v = r0 + g * 16 + ii;
+    const bool vok = v < r1;
     float gv[NEP];
 #pragma unroll
     for (int e = 0; e < NEP; ++e) gv[e] = bload4f(qr, qoff[e] + uint32_t(v) * 4u);
@@ -570,6 +566,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     for (int x = 0; x < NX1; ++x) xacc[x] = 0.f;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
+      if constexpr (FIRST) {
+        const uint4 gq = gsh[(kb + s * KS) / EPL];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) xf[t][s] = norm_pack<DT>(xf[t][s], gq, rt[t]);
+      }
       const uint4 f = fr[s % D];
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] = mfma_step<DT>(f, xf[t][s], acc[t]);
@@ -602,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       }
       const float z = float(zz);
       const bool valid = tok_ok[e] && vok;
-      zst[jj[e]][int(g - gb) * 16 + ii] = z;
+      zst[jj[e]][(g - gb) * 16 + ii] = z;
       if (a.stats) {
         Stat& S = st[e];
         const bool fin = fabsf(z) <= FLT_MAX;
@@ -618,10 +619,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
         }
       }
     }
-    if (g + 1 == g1 || int(g + 1 - gb) == SF) {  // write out the staged run
+    if (g + 1 == ng || g + 1 - gb == SF) {  // write out the staged run
       __syncthreads();
-      const int ncol = int(g + 1 - gb) * 16;
-      const uint32_t c0 = uint32_t(gb * 16);
+      const int64_t c0l = r0 + gb * 16;
+      const int ncol = int(min<int64_t>((g + 1 - gb) * 16, r1 - c0l));
+      const uint32_t c0 = uint32_t(c0l);
 #pragma unroll
       for (int rr = 0; rr < NTOK; ++rr) {
         if (rr >= a.rows) break;
@@ -633,7 +635,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       gb = g + 1;
     }
     buf ^= 1;
-  }
+  };
+  group(0, Tag<true>{});
+  for (int g = 1; g < ng; ++g) group(g, Tag<false>{});
 
   if (!a.stats) return;
 #pragma unroll
