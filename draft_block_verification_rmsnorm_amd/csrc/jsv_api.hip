@@ -226,21 +226,16 @@ jsv_status jsv_verify_sample(const jsv_lm_head* head, const void* hidden,
   f.n_accepted = n_accepted;
   f.committed = committed;
   f.flags = flags;
-  if (f.P <= 0 || launch_finalize(f, stream) != hipSuccess) return JSV_EHIP;
-  if (!(temperature > 0.f)) return JSV_OK;  // greedy: the bonus is the argmax, already written
+  if (f.P <= 0 || launch_rowstat(f, stream) != hipSuccess) return JSV_EHIP;
+  if (!(temperature > 0.f)) {  // greedy: the scan writes the argmax bonus
+    return launch_scan(f, stream) == hipSuccess ? JSV_OK : JSV_EHIP;
+  }
   SampleArgs a{};
-  a.V = head->vocab;
-  a.B = B;
-  a.K = K;
-  a.T = temperature;
+  a.f = f;
   a.c = kLog2e / temperature;
-  a.mode = mode;
   a.logits = logits_out ? logits_out : reinterpret_cast<const float*>(w + L.logits);
   a.G = draft_logits;
-  a.req = reinterpret_cast<const ReqState*>(w + L.req);
   a.zs = reinterpret_cast<double*>(w + L.zs);
-  a.committed = committed;
-  a.flags = flags;
   return launch_sample(a, stream) == hipSuccess ? JSV_OK : JSV_EHIP;
 }
 
@@ -293,7 +288,8 @@ jsv_status jsv_score_outcomes(const jsv_lm_head* head, const void* hidden_pred,
   f.out_token = out_token;
   f.out_prob = out_prob;
   f.len_marginal = len_marginal;
-  if (f.P <= 0 || launch_finalize(f, stream) != hipSuccess) return JSV_EHIP;
+  if (f.P <= 0 || launch_rowstat(f, stream) != hipSuccess || launch_scan(f, stream) != hipSuccess)
+    return JSV_EHIP;
   if (!(temperature > 0.f)) return JSV_OK;
   ScoreArgs a{};
   a.V = head->vocab;

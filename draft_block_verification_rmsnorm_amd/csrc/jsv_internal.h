@@ -165,17 +165,14 @@ struct FinalArgs {
   double* len_marginal;   // may be null
 };
 
+// Bonus sampler (T > 0 verification): both kernels run the acceptance scan of `f`
+// themselves, so the scan needs no launch of its own on this path.
 struct SampleArgs {
-  int64_t V;
-  int B, K;
-  float T, c;
-  int mode;
+  FinalArgs f;
+  float c;                // log2(e) / T
   const float* logits;
   const float* G;
-  const ReqState* req;
   double* zs;             // [B][slices][2]
-  int* committed;
-  uint32_t* flags;        // may be null
 };
 
 struct ScoreArgs {
@@ -201,7 +198,8 @@ struct ScoreArgs {
 // `nks` is hidden / (kWaves * elements per k-step); the launcher picks the instance.
 bool stats_supported(int dtype, int nks);
 hipError_t launch_stats(int dtype, int nks, int grid, const StatsArgs& a, hipStream_t stream);
-hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream);
+hipError_t launch_rowstat(const FinalArgs& a, hipStream_t stream);
+hipError_t launch_scan(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
 

@@ -760,31 +760,107 @@ __global__ __launch_bounds__(kWave) void rowstat_kernel(FinalArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kWave) void scan_kernel(FinalArgs a) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+// The acceptance scan of request b on one wave, lane i = row i (i <= K).  Every kernel
+// that runs it on the same inputs gets the same k: the rule is positional and the
+// uniforms are counter-based.
+struct Scan {
+  Stat st;        // this lane's row statistics
+  int di;         // this lane's draft token (-1 past the drafts)
+  double alpha;   // this lane's acceptance probability
+  bool bad;       // the request is invalid (same on every lane)
+  int k;          // first rejection, K if none (same on every lane)
+  double vk;      // bonus uniform of row k
+  uint32_t f;     // decision flags
+};
+
+__device__ Scan scan_request(const FinalArgs& a, int b) {
+  const int lane = threadIdx.x & (kWave - 1);
   const int K = a.K, R = K + 1;
   const int64_t V = a.V;
   const bool soft = a.T > 0.f;
   const double cd = soft ? kLog2eD / double(a.T) : 0.0;
-  const int di = (lane < K) ? a.drafts[b * K + lane] : -1;
+  Scan sc;
+  sc.di = (lane < K) ? a.drafts[b * K + lane] : -1;
   DraftLogit dl{};
   if (soft && lane < K) dl = a.dlog[b * R + lane];
-  // Lane i handles row i of request b.
+  const bool act = lane <= K;
+  stat_init(sc.st);
+  if (act) sc.st = stat_load(a.rowstat[b * R + lane]);
+  const Stat& st = sc.st;
+  const int di = sc.di;
+  sc.bad = __ballot(act && ((st.flags & JSV_FLAG_INVALID) || (lane < K && (di < 0 || (int64_t)di >= V)))) != 0;
+  sc.alpha = 0.0;
+  sc.k = K;
+  sc.vk = 0.0;
+  sc.f = 0;
+  if (sc.bad) return sc;
+  if (!soft) {
+    // Greedy verification: accept while the draft equals the row's argmax.
+    sc.alpha = (lane < K && di == st.idx) ? 1.0 : 0.0;
+  } else if (lane < K) {
+    const double pd = exp2((dl.z - double(st.m)) * cd) / st.s;
+    if (a.mode == JSV_PROPOSAL_POINT) {
+      sc.alpha = pd;
+    } else {
+      const double qd = exp2((double(dl.g) - double(st.mq)) * cd) / st.sq;
+      sc.alpha = (pd == 0.0) ? 0.0 : (pd >= qd ? 1.0 : pd / qd);
+    }
+  }
+  if (!soft) {
+    const uint64_t rej = __ballot(lane < K && sc.alpha == 0.0);
+    sc.k = rej ? __builtin_ctzll(rej) : K;
+    const bool gap = act && lane <= sc.k && (st.m - st.top2) < kLogitGapTie;
+    if (__ballot(gap)) sc.f |= JSV_FLAG_LOGIT_GAP;
+  } else if (a.kind == kFinalizeVerify) {
+    double u = 0.0, v = 0.0;
+    if (act) row_uniforms(a.seed, a.offset, b, lane, u, v);
+    const uint64_t rej = __ballot(lane < K && !(u < sc.alpha));
+    sc.k = rej ? __builtin_ctzll(rej) : K;
+    const bool tie = lane < K && lane <= sc.k && fabs(u - sc.alpha) < kAcceptTie;
+    if (__ballot(tie)) sc.f |= JSV_FLAG_ACCEPT_TIE;
+    sc.vk = readlane_d(v, sc.k);
+  }
+  return sc;
+}
+
+// Row k's statistics with the scan result (what the bonus sampler needs of the rule).
+__device__ inline ReqState req_state(const FinalArgs& a, const Scan& sc) {
+  ReqState rq{};
+  if (sc.bad) {
+    rq.k = -1; rq.dk = -1; rq.flags = JSV_FLAG_INVALID;
+    return rq;
+  }
+  const int k = sc.k, K = a.K;
+  rq.vk = sc.vk; rq.k = k; rq.flags = sc.f;
+  rq.s = readlane_d(sc.st.s, k); rq.sq = readlane_d(sc.st.sq, k);
+  rq.m = readlane_f(sc.st.m, k); rq.mq = readlane_f(sc.st.mq, k);
+  const int dk = readlane_i(sc.di, k);
+  rq.use_q = (a.mode == JSV_PROPOSAL_SOFTMAX && k < K) ? 1 : 0;
+  rq.dk = (a.mode == JSV_PROPOSAL_POINT && k < K) ? dk : -1;
+  return rq;
+}
+
+// Per-request outputs of verification: committed = d_0..d_{k-1}, bonus, then -1.
+__device__ inline void write_verify(const FinalArgs& a, int b, const Scan& sc, int bonus, uint32_t f) {
+  const int lane = threadIdx.x & (kWave - 1), K = a.K, row = b * (K + 1) + lane;
+  if (lane <= K) a.committed[row] = sc.bad ? -1 : ((lane < sc.k) ? sc.di : (lane == sc.k ? bonus : -1));
+  if (lane == 0) {
+    a.n_accepted[b] = sc.bad ? -1 : sc.k;
+    if (a.flags) a.flags[b] = sc.bad ? uint32_t(JSV_FLAG_INVALID) : f;
+  }
+}
+
+__global__ __launch_bounds__(kWave) void scan_kernel(FinalArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int K = a.K, R = K + 1;
+  const bool soft = a.T > 0.f;
   const bool act = lane <= K;
   const int row = b * R + lane;
-  Stat st;
-  stat_init(st);
-  if (act) st = stat_load(a.rowstat[row]);
-  const bool bad = act && ((st.flags & JSV_FLAG_INVALID) || (lane < K && (di < 0 || (int64_t)di >= V)));
-  if (__ballot(bad) != 0) {
-    if (act && a.kind == kFinalizeVerify) a.committed[row] = -1;
-    if (lane == 0) {
-      if (a.kind == kFinalizeVerify) a.n_accepted[b] = -1;
-      if (a.flags) a.flags[b] = JSV_FLAG_INVALID;
-      ReqState rq{};
-      rq.k = -1; rq.dk = -1; rq.flags = JSV_FLAG_INVALID;
-      a.req[b] = rq;
-    }
+  const Scan sc = scan_request(a, b);
+  const ReqState rq = req_state(a, sc);
+  if (lane == 0) a.req[b] = rq;
+  if (sc.bad) {
+    if (a.kind == kFinalizeVerify) write_verify(a, b, sc, -1, 0u);
     if (a.kind == kFinalizeScore) {
       if (lane < a.top_n) {
         a.out_len[b * a.top_n + lane] = -1;
@@ -792,42 +868,13 @@ __global__ __launch_bounds__(kWave) void scan_kernel(FinalArgs a) {
         a.out_prob[b * a.top_n + lane] = 0.f;
       }
       if (act && a.len_marginal) a.len_marginal[row] = 0.0;
+      if (lane == 0 && a.flags) a.flags[b] = JSV_FLAG_INVALID;
     }
     return;
   }
-
-  double alpha = 0.0;
-  if (!soft) {
-    // Greedy verification: accept while the draft equals the row's argmax.
-    alpha = (lane < K && di == st.idx) ? 1.0 : 0.0;
-  } else if (lane < K) {
-    const double pd = exp2((dl.z - double(st.m)) * cd) / st.s;
-    if (a.mode == JSV_PROPOSAL_POINT) {
-      alpha = pd;
-    } else {
-      const double qd = exp2((double(dl.g) - double(st.mq)) * cd) / st.sq;
-      alpha = (pd == 0.0) ? 0.0 : (pd >= qd ? 1.0 : pd / qd);
-    }
-  }
-
-  uint32_t f = 0;
-  int k = K;
-  double vk = 0.0;
-  if (!soft) {
-    const uint64_t rej = __ballot(lane < K && alpha == 0.0);
-    k = rej ? __builtin_ctzll(rej) : K;
-    const bool gap = act && lane <= k && (st.m - st.top2) < kLogitGapTie;
-    if (__ballot(gap)) f |= JSV_FLAG_LOGIT_GAP;
-  } else if (a.kind == kFinalizeVerify) {
-    double u = 0.0, v = 0.0;
-    if (act) row_uniforms(a.seed, a.offset, b, lane, u, v);
-    const uint64_t rej = __ballot(lane < K && !(u < alpha));
-    k = rej ? __builtin_ctzll(rej) : K;
-    const bool tie = lane < K && lane <= k && fabs(u - alpha) < kAcceptTie;
-    if (__ballot(tie)) f |= JSV_FLAG_ACCEPT_TIE;
-    vk = readlane_d(v, k);
-  }
-  const int bonus = readlane_i(st.idx, k);
+  const int k = sc.k;
+  const double alpha = sc.alpha;
+  const int bonus = readlane_i(sc.st.idx, k);
 
   // A_i = prod_{j<i} alpha_j (probability of reaching row i).
   double A = 1.0;
@@ -835,28 +882,17 @@ __global__ __launch_bounds__(kWave) void scan_kernel(FinalArgs a) {
     const double aj = readlane_d(alpha, j);
     if (j < lane) A *= aj;
   }
-
   if (act) {
+    const Stat& st = sc.st;
     RowFinal rf{};
     rf.s = st.s; rf.sq = st.sq; rf.alpha = alpha; rf.A = A;
     rf.m = st.m; rf.top2 = st.top2; rf.mq = st.mq; rf.idx = st.idx; rf.flags = st.flags;
     a.rowfinal[row] = rf;
   }
-  // Row k's statistics travel with the scan result: the bonus sampler reads nothing else.
-  ReqState rq{};
-  rq.vk = vk; rq.k = k; rq.flags = f;
-  rq.s = readlane_d(st.s, k); rq.sq = readlane_d(st.sq, k);
-  rq.m = readlane_f(st.m, k); rq.mq = readlane_f(st.mq, k);
-  const int dk = readlane_i(di, k);
-  rq.use_q = (a.mode == JSV_PROPOSAL_SOFTMAX && k < K) ? 1 : 0;
-  rq.dk = (a.mode == JSV_PROPOSAL_POINT && k < K) ? dk : -1;
   if (a.kind == kFinalizeVerify) {
-    if (act) a.committed[row] = (lane < k) ? di : ((lane == k && !soft) ? bonus : -1);
-    if (lane == 0) {
-      a.n_accepted[b] = k;
-      if (a.flags) a.flags[b] = f;
-      a.req[b] = rq;
-    }
+    // T = 0: the bonus is the argmax of row k.  T > 0 verification draws it in the
+    // sampler kernels, which run this scan themselves.
+    write_verify(a, b, sc, soft ? -1 : bonus, sc.f);
   } else {  // score
     if (act && a.len_marginal) {
       a.len_marginal[row] = soft ? ((lane < K) ? A * (1.0 - alpha) : A) : (lane == k ? 1.0 : 0.0);
@@ -866,10 +902,7 @@ __global__ __launch_bounds__(kWave) void scan_kernel(FinalArgs a) {
       a.out_token[b * a.top_n + lane] = (lane == 0) ? bonus : -1;
       a.out_prob[b * a.top_n + lane] = (lane == 0) ? 1.f : 0.f;
     }
-    if (lane == 0) {
-      if (a.flags) a.flags[b] = f;
-      a.req[b] = rq;
-    }
+    if (lane == 0 && a.flags) a.flags[b] = sc.f;
   }
 }
 
@@ -925,11 +958,17 @@ __device__ inline RowModel req_model(const ReqState& rq, float c) {
 // target mass, for the zero-residual fallback) of row k over each slice.
 __global__ __launch_bounds__(kSliceThreads) void slice_sum_kernel(SampleArgs a) {
   const int b = blockIdx.y, j = blockIdx.x, tid = threadIdx.x, NB = gridDim.x;
-  const ReqState rq = a.req[b];
-  if (!(a.T > 0.f) || rq.k < 0) return;
-  const int K = a.K, k = rq.k, row = b * (K + 1) + k;
+  __shared__ ReqState rq_sh;
+  if (tid < kWave) {
+    const ReqState r = req_state(a.f, scan_request(a.f, b));
+    if (tid == 0) rq_sh = r;
+  }
+  __syncthreads();
+  const ReqState rq = rq_sh;
+  if (rq.k < 0) return;
+  const int K = a.f.K, k = rq.k, row = b * (K + 1) + k;
   const RowModel rm = req_model(rq, a.c);
-  const int64_t V = a.V;
+  const int64_t V = a.f.V;
   const uint32_t rowbytes = uint32_t(V) * 4u;
   const rsrc_t zr = make_rsrc(a.logits + (size_t)row * V, rowbytes);
   const rsrc_t gr = make_rsrc(rm.use_q ? a.G + (size_t)(b * K + k) * V : a.logits,
@@ -972,7 +1011,7 @@ constexpr int kLocRounds = 4;  // slice-total rounds kept in registers (V <= 262
 __global__ __launch_bounds__(kWave) void locate_kernel(SampleArgs a) {
   constexpr int CR = kSampleSlice / kWave;  // column rounds inside a slice
   const int b = blockIdx.x, lane = threadIdx.x;
-  const int NB = sample_slices(a.V), rounds = (NB + kWave - 1) / kWave;
+  const int NB = sample_slices(a.f.V), rounds = (NB + kWave - 1) / kWave;
   const rsrc_t zsr = make_rsrc(a.zs + (size_t)b * NB * 2, uint64_t(NB) * 16u);
   uint4 pre[kLocRounds];
 #pragma unroll
@@ -985,11 +1024,15 @@ __global__ __launch_bounds__(kWave) void locate_kernel(SampleArgs a) {
     if (q >= kLocRounds) x = bload16(zsr, uint32_t(q * kWave + lane) * 16u, 0);
     return x;
   };
-  const ReqState rq = a.req[b];
-  if (!(a.T > 0.f) || rq.k < 0) return;
-  const int K = a.K, k = rq.k, row = b * (K + 1) + k;
+  const Scan sc = scan_request(a.f, b);
+  if (sc.bad) {
+    write_verify(a.f, b, sc, -1, 0u);
+    return;
+  }
+  const ReqState rq = req_state(a.f, sc);
+  const int K = a.f.K, k = rq.k, row = b * (K + 1) + k;
   const RowModel rm = req_model(rq, a.c);
-  const int64_t V = a.V;
+  const int64_t V = a.f.V;
 
   // pass 1: both totals
   double Zr = 0.0, Zp = 0.0;
@@ -1067,10 +1110,7 @@ __global__ __launch_bounds__(kWave) void locate_kernel(SampleArgs a) {
     tok = lastpos;
     f |= JSV_FLAG_CDF_TIE;
   }
-  if (lane == 0) {
-    a.committed[row] = tok;
-    if (a.flags) a.flags[b] |= f;
-  }
+  write_verify(a.f, b, sc, tok, sc.f | f);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1298,21 +1338,23 @@ hipError_t launch_stats(int dtype, int nks, int grid, const StatsArgs& a, hipStr
                            : dispatch_rows<JSV_F32>(nks, grid, a, stream);
 }
 
-hipError_t launch_finalize(const FinalArgs& a, hipStream_t stream) {
+hipError_t launch_rowstat(const FinalArgs& a, hipStream_t stream) {
   const int tasks = (a.T > 0.f ? a.K : 0) + a.K + 1;
   hipLaunchKernelGGL(rowstat_kernel, dim3(tasks, a.B), dim3(kWave), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const FinalArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(scan_kernel, dim3(a.B), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(slice_sum_kernel, dim3(sample_slices(a.V), a.B), dim3(kSliceThreads), 0,
+  hipLaunchKernelGGL(slice_sum_kernel, dim3(sample_slices(a.f.V), a.f.B), dim3(kSliceThreads), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(locate_kernel, dim3(a.B), dim3(kWave), 0, stream, a);
+  hipLaunchKernelGGL(locate_kernel, dim3(a.f.B), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
