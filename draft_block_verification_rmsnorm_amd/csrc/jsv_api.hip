@@ -53,29 +53,17 @@ jsv_status check_block(int32_t B, int32_t K, float T, int32_t mode) {
 }
 
 // Workgroups of the LM-head kernel: one per CU, at most one per 16-row vocabulary group.
-int stats_grid(int64_t V) {
-  const int cus = device_cu_count();
-  if (cus <= 0) return 0;
-  int64_t grid = cus < kMaxGrid ? cus : kMaxGrid;
-  const int64_t ngroups = (V + 15) / 16;
-  return int(grid > ngroups ? ngroups : grid);
-}
-
-// One or more passes of the LM-head kernel over W, kRowsPerPass rows each.
 jsv_status run_stats(const jsv_lm_head* head, int nks, const void* hidden, int M, float* logits,
                      const float* G, int B, int K, float T, int mode, int stats, RowStat* partial,
                      float* rnorm, hipStream_t stream) {
-  const int grid = stats_grid(head->vocab);
-  if (grid <= 0) return JSV_EHIP;
+  const int cus = device_cu_count();
+  if (cus <= 0) return JSV_EHIP;
   StatsArgs a{};
   a.W = head->weight;
   a.gamma = head->norm_weight;
-  a.hidden = hidden;
   a.V = head->vocab;
   a.d = int(head->hidden);
-  a.M = M;
   a.eps = head->eps;
-  a.logits = logits;
   a.G = G;
   a.B = B;
   a.K = K;
@@ -85,10 +73,19 @@ jsv_status run_stats(const jsv_lm_head* head, int nks, const void* hidden, int M
   a.want_q = (stats && mode == JSV_PROPOSAL_SOFTMAX && T > 0.f && G != nullptr) ? 1 : 0;
   a.partial = partial;
   a.rnorm = rnorm;
-  for (int row0 = 0; row0 < M; row0 += kRowsPerPass) {
-    a.row0 = row0;
-    a.rows = (M - row0) < kRowsPerPass ? (M - row0) : kRowsPerPass;
-    if (launch_stats(head->dtype, nks, grid, a, stream) != hipSuccess) return JSV_EHIP;
+  // Verification and scoring fit one launch; plain logits of many rows take several.
+  const size_t rowbytes = size_t(head->hidden) * (head->dtype == JSV_BF16 ? 2 : 4);
+  for (int m0 = 0; m0 < M; m0 += kMaxPlanRows) {
+    const int m = (M - m0) < kMaxPlanRows ? (M - m0) : kMaxPlanRows;
+    if (stats && m0 > 0) return JSV_EUNSUPPORTED;
+    const StatsPlan pl = plan_stats(head->vocab, m, cus);
+    a.hidden = static_cast<const char*>(hidden) + size_t(m0) * rowbytes;
+    a.logits = logits + size_t(m0) * size_t(head->vocab);
+    a.M = m;
+    a.rp = pl.rp;
+    a.npass = pl.npass;
+    a.nchunk = pl.nchunk;
+    if (launch_stats(head->dtype, nks, pl.nchunk * pl.npass, a, stream) != hipSuccess) return JSV_EHIP;
   }
   return JSV_OK;
 }
@@ -110,7 +107,8 @@ FinalArgs final_args(const jsv_lm_head* head, const void* hidden, const int32_t*
   f.T = T;
   f.mode = mode;
   f.kind = kind;
-  f.P = stats_grid(head->vocab);
+  const int cus = device_cu_count();
+  f.P = cus > 0 ? plan_stats(head->vocab, B * (K + 1), cus).nchunk : 0;
   f.partial = reinterpret_cast<const RowStat*>(ws + L.partial);
   f.rowstat = reinterpret_cast<RowStat*>(ws + L.rowstat);
   f.dlog = reinterpret_cast<DraftLogit*>(ws + L.dlog);

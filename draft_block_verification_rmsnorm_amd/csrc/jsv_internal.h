@@ -109,14 +109,16 @@ inline WsLayout ws_layout(int64_t V, int B, int K, int top_n) {
   return L;
 }
 
-// Fused RMSNorm + LM head + statistics, one pass over W for rows [row0, row0 + rows).
+// Fused RMSNorm + LM head + statistics of M rows in one launch of nchunk * npass
+// workgroups: the rows are split into npass passes of rp rows (rp <= kRowsPerPass) and
+// the vocabulary into nchunk chunks.
 struct StatsArgs {
   const void* W;          // [V][d]
   const void* gamma;      // [d]
   const void* hidden;     // [M][d]
   int64_t V;
   int d;
-  int row0, rows;         // rows handled by this pass (rows <= kRowsPerPass)
+  int rp, npass, nchunk;  // rows per pass, passes, vocabulary chunks
   int M;                  // total rows
   float eps;
   float* logits;          // [M][V]
@@ -125,9 +127,27 @@ struct StatsArgs {
   float T, c;             // temperature and log2(e) / T
   int stats;              // write per-row partial statistics
   int want_q;             // also draft-logit statistics (softmax proposal, T > 0)
-  RowStat* partial;       // [M][gridDim]
+  RowStat* partial;       // [M][nchunk]
   float* rnorm;           // [M] RMSNorm factor of every row (written by workgroup 0), or null
 };
+
+// Launch plan of the LM-head kernel for M <= 8 * kRowsPerPass rows: the fewest passes
+// (a power of two, so that the passes of a chunk share an XCD) and as many vocabulary
+// chunks as leave one workgroup per compute unit.
+struct StatsPlan {
+  int npass, rp, nchunk;
+};
+inline StatsPlan plan_stats(int64_t V, int M, int cus) {
+  StatsPlan p{1, M, 1};
+  while ((M + p.npass - 1) / p.npass > kRowsPerPass) p.npass *= 2;
+  p.rp = (M + p.npass - 1) / p.npass;
+  int64_t base = cus < kMaxGrid ? cus : kMaxGrid;
+  const int64_t ngroups = (V + 15) / 16;
+  if (base > ngroups) base = ngroups;
+  p.nchunk = int(base / p.npass > 0 ? base / p.npass : 1);
+  return p;
+}
+constexpr int kMaxPlanRows = 8 * kRowsPerPass;  // verification and scoring: B (K + 1) <= 264
 
 enum FinalizeKind { kFinalizeVerify = 1, kFinalizeScore = 2 };
 

@@ -367,11 +367,12 @@ __device__ inline void fold(float& m, double& s, float ze, float c) {
   m = nm;
 }
 
-// Prefetch window: the largest divisor of NKS whose W registers fit beside the
-// normalised hidden states (160 of the 256 VGPRs a wave has at 2 waves per SIMD).
+// Prefetch window in k-steps: half a group of W ahead for one tile (measured faster than
+// a whole group, whose registers crowd the rest of the loop), at most 8 steps for two.
 constexpr int pick_window(int NT, int NKS) {
-  for (int D = NKS; D >= 1; --D)
-    if (NKS % D == 0 && NT * NKS * 4 + 4 * D <= 160) return D;
+  const int cap = NT <= 1 ? NKS / 2 : 8;
+  for (int D = cap; D >= 1; --D)
+    if (NKS % D == 0) return D;
   return 1;
 }
 
@@ -416,7 +417,25 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   __shared__ float rnorm[kRowsPerPass];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int P = gridDim.x, wg = blockIdx.x;
+  // Workgroup -> (vocabulary chunk, pass of rows).  The passes of one chunk sit on the
+  // same XCD (workgroups are dealt to the 8 XCDs round robin), so W is read from HBM once
+  // and the other passes find it in that XCD's L2.
+  int pass, chunk;
+  {
+    const int x = blockIdx.x, grid = gridDim.x, np = a.npass;
+    if (grid % (8 * np) == 0) {
+      const int slot = x >> 3, cpx = (grid >> 3) / np;
+      chunk = (x & 7) * cpx + slot / np;
+      pass = slot % np;
+    } else {
+      chunk = x / np;
+      pass = x % np;
+    }
+  }
+  const int row0 = pass * a.rp;
+  const int rows = min(a.rp, a.M - row0);
+  if (rows <= 0) return;
+  const int P = a.nchunk, wg = chunk;
   const int64_t V = a.V;
   const int d = a.d;
   const int64_t r0 = V * wg / P, r1 = V * (wg + 1) / P;  // this workgroup's vocabulary rows
@@ -435,8 +454,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   // ---- RMSNorm of the rows of this pass ----------------------------------------------
   // The hidden-state and gamma loads are issued before the first W loads: a wave's
   // loads return in issue order, so the norm does not wait behind W.
-  const char* Hb = static_cast<const char*>(a.hidden) + (size_t)a.row0 * rowbytes;
-  const rsrc_t hr = make_rsrc(Hb, (uint64_t)a.rows * rowbytes);
+  const char* Hb = static_cast<const char*>(a.hidden) + (size_t)row0 * rowbytes;
+  const rsrc_t hr = make_rsrc(Hb, (uint64_t)rows * rowbytes);
   const rsrc_t gr = make_rsrc(a.gamma, rowbytes);
   uint4 gq[XPT];
 #pragma unroll
@@ -448,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
   for (int t = 0; t < NT1; ++t) {
     const int tok = t * 16 + (lane & 15);
-    tokoff[t] = (t < NT && tok < a.rows) ? uint32_t(tok) * rowbytes : kOutOfRange;
+    tokoff[t] = (t < NT && tok < rows) ? uint32_t(tok) * rowbytes : kOutOfRange;
   }
   uint4 xf[NT1][NKS];  // this wave's slice of the tile tokens (padding tokens read zeros)
 #pragma unroll
@@ -492,13 +511,13 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     if (lane == 0) ssq[w][NT * 16 + x] = ps;
   }
   __syncthreads();
-  if (tid < a.rows) {
+  if (tid < rows) {
     double ss = 0.0;
 #pragma unroll
     for (int w2 = 0; w2 < kWaves; ++w2) ss += ssq[w2][tid];  // fixed order over waves
     const float r = rms_factor(ss, d, a.eps);
     rnorm[tid] = r;
-    if (wg == 0 && a.rnorm != nullptr) a.rnorm[a.row0 + tid] = r;
+    if (wg == 0 && a.rnorm != nullptr) a.rnorm[row0 + tid] = r;
   }
   __syncthreads();
 
@@ -509,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
   for (int t = 0; t < NT1; ++t) {
     const int tok = t * 16 + (lane & 15);
-    rt[t] = (t < NT && tok < a.rows) ? rnorm[tok] : 0.f;
+    rt[t] = (t < NT && tok < rows) ? rnorm[tok] : 0.f;
   }
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
@@ -527,9 +546,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   const bool soft = a.T > 0.f;
   const float c = a.c;
   // Logits rows of this pass, and the draft-logit rows of the requests it touches.
-  const rsrc_t lr = make_rsrc(a.logits + (size_t)a.row0 * V, (uint64_t)a.rows * (uint64_t)V * 4u);
-  const int qrow0 = a.want_q ? (a.row0 / (a.K + 1)) * a.K : 0;
-  const int qrows = a.want_q ? ((a.row0 + a.rows - 1) / (a.K + 1)) * a.K + a.K - qrow0 : 0;
+  const rsrc_t lr = make_rsrc(a.logits + (size_t)row0 * V, (uint64_t)rows * (uint64_t)V * 4u);
+  const int qrow0 = a.want_q ? (row0 / (a.K + 1)) * a.K : 0;
+  const int qrows = a.want_q ? ((row0 + rows - 1) / (a.K + 1)) * a.K + a.K - qrow0 : 0;
   const rsrc_t qr = make_rsrc(a.G + (size_t)qrow0 * V, (uint64_t)qrows * (uint64_t)V * 4u);
   int jj[NEP];
   bool tok_ok[NEP], qrow[NEP];
@@ -538,8 +557,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
   for (int e = 0; e < NEP; ++e) {
     jj[e] = (tid >> 4) + 32 * e;
-    tok_ok[e] = jj[e] < NTOK && jj[e] < a.rows;
-    const int row = a.row0 + (tok_ok[e] ? jj[e] : 0);
+    tok_ok[e] = jj[e] < NTOK && jj[e] < rows;
+    const int row = row0 + (tok_ok[e] ? jj[e] : 0);
     qrow[e] = false;
     qoff[e] = kOutOfRange;
     if (a.want_q && tok_ok[e]) {
@@ -626,7 +645,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       const uint32_t c0 = uint32_t(c0l);
 #pragma unroll
       for (int rr = 0; rr < NTOK; ++rr) {
-        if (rr >= a.rows) break;
+        if (rr >= rows) break;
         for (int cc = tid; cc < ncol; cc += kThreads) {
           const uint32_t vv = c0 + uint32_t(cc);
           bstore4f_nt(zst[rr][cc], lr, vv < uint32_t(V) ? uint32_t(rr) * uint32_t(V) * 4u + vv * 4u : kOutOfRange);
@@ -647,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       RowStat rs;
       rs.s = st[e].s; rs.sq = st[e].sq; rs.m = st[e].m; rs.top2 = st[e].top2; rs.mq = st[e].mq;
       rs.idxf = (uint32_t(st[e].idx) & kIdxMask) | (st[e].flags ? kBadBit : 0u);
-      a.partial[(size_t)(a.row0 + jj[e]) * P + wg] = rs;
+      a.partial[(size_t)(row0 + jj[e]) * P + wg] = rs;
     }
   }
 }
@@ -1324,7 +1343,7 @@ static hipError_t dispatch_nks(int nks, int grid, const StatsArgs& a, hipStream_
 // when exactly one row is left over.
 template <int DT>
 static hipError_t dispatch_rows(int nks, int grid, const StatsArgs& a, hipStream_t s) {
-  const int rows = a.rows;
+  const int rows = a.rp;
   if (rows <= 1) return dispatch_nks<DT, 0, 1>(nks, grid, a, s);
   if (rows <= 16) return dispatch_nks<DT, 1, 0>(nks, grid, a, s);
   if (rows == 17) return dispatch_nks<DT, 1, 1>(nks, grid, a, s);
@@ -1333,7 +1352,9 @@ static hipError_t dispatch_rows(int nks, int grid, const StatsArgs& a, hipStream
 }
 
 hipError_t launch_stats(int dtype, int nks, int grid, const StatsArgs& a, hipStream_t stream) {
-  if (a.rows < 1 || a.rows > kRowsPerPass) return hipErrorInvalidValue;
+  if (a.rp < 1 || a.rp > kRowsPerPass || a.npass < 1 || a.nchunk < 1 || grid != a.nchunk * a.npass ||
+      a.M > a.rp * a.npass)
+    return hipErrorInvalidValue;
   return dtype == JSV_BF16 ? dispatch_rows<JSV_BF16>(nks, grid, a, stream)
                            : dispatch_rows<JSV_F32>(nks, grid, a, stream);
 }
