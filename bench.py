@@ -46,6 +46,11 @@ def algorithmic_bytes(cfg, T, mode_softmax):
     return b
 
 
+def lmhead_flops(cfg):
+    """Dense flops of the LM-head product of one call: 2 M V d."""
+    return 2 * cfg.batch * (cfg.K + 1) * cfg.vocab * cfg.hidden
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -208,6 +213,9 @@ def main():
                      "traffic": measured_traffic(args.config) if (T > 0 and not args.point) else None,
                      "kernel": "stats_kernel (fused RMSNorm + LM head + softmax statistics)",
                      "algorithmic_bytes": abytes},
+        "mfma": {"achieved": round(lmhead_flops(cfg) / (k1_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(lmhead_flops(cfg) / (k1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 "flops": lmhead_flops(cfg)},
         "accepted_last_step": n_acc,
     }
     if not args.no_cpu_baseline:

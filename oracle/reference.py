@@ -391,3 +391,121 @@ def score_outcomes(head, hidden_pred, draft_tokens, draft_logits, T, mode, N):
 def lmhead_logits(head, hidden_rows):
     """RMSNorm + LM head for rows [M, d] -> float64 logits [M, V]."""
     return block_logits(head, hidden_rows)
+
+
+# ---- next rows: anchor replacement, cache lookup, calibrated lengths, SSD fan-out --------
+def anchor_replace(head, hidden_pred, draft_tokens):
+    """Anchor replacement (paper §4.3 "Anchor Replacement"): the decoder reads the
+    predicted states of the block and finds the first position at which its most likely
+    token differs from the draft; that token is written there.
+
+    hidden_pred [B, K+1, d]; draft_tokens [B, K].  Returns position [B] (first i < K with
+    argmax z_i != d_i, or K when every draft matches), token [B] (the argmax of that row;
+    the argmax of row K when every draft matches) and flags [B] (LOGIT_GAP when a row up
+    to the position has a top-2 gap < 1e-3; INVALID for non-finite logits or a draft
+    outside the vocabulary, with position = token = -1).  Ties go to the lowest id.
+    """
+    drafts = np.asarray(draft_tokens)
+    B, K = drafts.shape
+    z = block_logits(head, hidden_pred)
+    V = z.shape[-1]
+    pos = np.full(B, -1, np.int64)
+    tok = np.full(B, -1, np.int64)
+    flags = np.zeros(B, np.int64)
+    for b in range(B):
+        if (not np.all(np.isfinite(z[b]))) or any(not (0 <= int(x) < V) for x in drafts[b]):
+            flags[b] = FLAG_INVALID
+            continue
+        am = [int(np.argmax(z[b, i])) for i in range(K + 1)]
+        k = next((i for i in range(K) if am[i] != int(drafts[b, i])), K)
+        pos[b], tok[b] = k, am[k]
+        if any(top2_gap(z[b, i]) < LOGIT_GAP_TIE for i in range(k + 1)):
+            flags[b] = FLAG_LOGIT_GAP
+    return pos, tok, flags
+
+
+def cache_lookup(n_accepted, committed, out_len, out_token):
+    """Cache hit test (paper §4.1): the realised outcome of a round is (k, a) with k the
+    accepted count and a the bonus token committed at position k; it hits when it is one
+    of the cached (length, token) pairs.  Returns the index of the first matching entry per
+    request, or -1 (a miss, or an invalid round with k < 0)."""
+    n_accepted = np.asarray(n_accepted)
+    committed = np.asarray(committed)
+    out_len, out_token = np.asarray(out_len), np.asarray(out_token)
+    res = np.full(n_accepted.shape[0], -1, np.int64)
+    for b in range(n_accepted.shape[0]):
+        k = int(n_accepted[b])
+        if k < 0:
+            continue
+        a = int(committed[b, k])
+        for i in range(out_len.shape[1]):
+            if int(out_len[b, i]) == k and int(out_token[b, i]) == a:
+                res[b] = i
+                break
+    return res
+
+
+def calibrated_lengths(p_tilde):
+    """Calibrated length score (paper App. B.1, Eq. 12): with per-position estimates p~_i
+    for the 1-based positions i = 1..K of a block, G(k) = prod_{i <= k} p~_i (G(0) = 1) and
+    P~(k) = G(k) - G(k+1) for k = 0..K, with G(K+1) = 0.
+
+    p_tilde [B, K] in [0, 1] -> (scores [B, K+1] float64, flags [B]); a request with an
+    estimate outside [0, 1] (or not a number) is flagged INVALID and scored 0."""
+    p = np.asarray(p_tilde, dtype=np.float64)
+    B, K = p.shape
+    out = np.zeros((B, K + 1))
+    flags = np.zeros(B, np.int64)
+    for b in range(B):
+        if not np.all((p[b] >= 0.0) & (p[b] <= 1.0)):
+            flags[b] = FLAG_INVALID
+            continue
+        G = [1.0]
+        for i in range(K):
+            G.append(G[-1] * p[b, i])
+        G.append(0.0)
+        out[b] = [G[k] - G[k + 1] for k in range(K + 1)]
+    return out, flags
+
+
+def ssd_length_law(alpha, gamma):
+    """P_alpha(k) of the fan-out model (paper App. F.2): alpha^k (1 - alpha) for k < gamma,
+    alpha^gamma for k = gamma."""
+    return np.array([alpha ** k * (1.0 - alpha) for k in range(gamma)] + [alpha ** gamma])
+
+
+def fanout_objective(P, F, rho):
+    """Surrogate hit mass sum_k P(k) (1 - F_k^-rho) over active lengths (F_k >= 1)."""
+    return float(sum(P[k] * (1.0 - F[k] ** (-rho)) for k in range(len(P)) if F[k] >= 1.0))
+
+
+def geometric_fanout(alpha, rho, gamma, B):
+    """SSD's geometric fan-out as the maximiser of the surrogate problem (paper App. F.2,
+    Proposition 2(a) and its proof): the active lengths are the M lengths of largest
+    P_alpha(k) for some M (ties to the lower k); on them F_k = B P^(1/(1+rho)) / sum P^(1/(1+rho));
+    a candidate counts only when every active F_k >= 1, and the best candidate maximises
+    sum_k P(k) (1 - F_k^-rho).  The integer allocation rounds F down and hands the
+    remaining anchors to the largest remainders (ties to the lower k), as the paper does
+    for its Table 11.
+
+    Returns (F_real [gamma+1], F_int [gamma+1], hit_mass of F_real, active M)."""
+    P = ssd_length_law(alpha, gamma)
+    order = sorted(range(gamma + 1), key=lambda k: (-P[k], k))
+    best = None
+    for M in range(1, gamma + 2):
+        act = order[:M]
+        w = np.array([P[k] ** (1.0 / (1.0 + rho)) for k in act])
+        F = np.zeros(gamma + 1)
+        F[act] = B * w / w.sum()
+        if np.any(F[act] < 1.0):
+            continue
+        obj = fanout_objective(P, F, rho)
+        if best is None or obj > best[0]:
+            best = (obj, F, M)
+    obj, F, M = best
+    Fi = np.floor(F).astype(np.int64)
+    rem = B - int(Fi.sum())
+    frac = sorted(range(gamma + 1), key=lambda k: (-(F[k] - Fi[k]), k))
+    for k in frac[:rem]:
+        Fi[k] += 1
+    return F, Fi, obj, M

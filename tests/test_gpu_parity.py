@@ -175,6 +175,54 @@ def test_verify_d5120(dev):
     assert st["exact"] >= 4
 
 
+def test_sampler_law_point_mass_any_draft(tiny, dev):
+    """Losslessness through the GPU sampler itself: with the point-mass proposal the token
+    committed at row 0 is distributed as p_0 for any fixed draft (App. F.3), so over many
+    Philox offsets its histogram must pass a chi-square test against the oracle's p_0."""
+    from scipy import stats as sps
+    cfg = synth.CONFIGS["tiny"]
+    B, K, T = 8, cfg.K, 1.0
+    blk = synth.make_block(tiny.cpu, 1, K, cfg.sigma, T, seed=777)
+    hid = blk.hidden.expand(B, -1, -1).contiguous().to(dev)
+    drafts = blk.draft_tokens.expand(B, -1).contiguous().to(dev)
+    ws = jsv.new_workspace(tiny.gpu, B, K)
+    out = jsv.VerifyOut(B, K, dev)
+    calls = 3000
+    toks = torch.empty(calls, B, dtype=torch.int32, device=dev)
+    say(f"sampler law: {calls} calls x {B} requests")
+    for off in range(calls):
+        jsv.verify_block(tiny.gpu, hid, drafts, None, T, POINT, 5, off, ws, out=out)
+        toks[off] = out.committed[:, 0]
+    torch.cuda.synchronize()
+    t = toks.cpu().numpy().ravel()
+    z0 = oracle.block_logits(tiny.oh, blk.hidden[0, :1])[0]
+    p0 = oracle.probs(z0, T)
+    n = t.size
+    counts = np.bincount(t, minlength=p0.size).astype(np.float64)
+    exp = p0 * n
+    big = exp >= 5.0
+    obs = np.append(counts[big], counts[~big].sum())
+    ex = np.append(exp[big], exp[~big].sum())
+    chi2 = float(((obs - ex) ** 2 / ex).sum())
+    pval = float(sps.chi2.sf(chi2, obs.size - 1))
+    say(f"  chi2 {chi2:.1f} on {obs.size - 1} dof, p = {pval:.3g}; draft token mass {p0[int(drafts[0, 0])]:.3f}")
+    assert pval > 1e-4
+
+
+def test_score_marginals_sum_to_one(tiny, dev):
+    """P(k) over k = 0..K telescopes to 1 (§4.2 Eq. 6), on the GPU's own float64 products."""
+    cfg = synth.CONFIGS["tiny"]
+    ws = jsv.new_workspace(tiny.gpu, 8, cfg.K, 8)
+    for mode in (SOFT, POINT):
+        blk = synth.make_block(tiny.cpu, 8, cfg.K, cfg.sigma, 1.0, seed=4242 + mode)
+        out = jsv.score_outcomes(tiny.gpu, blk.hidden.to(dev), blk.draft_tokens.to(dev),
+                                 blk.draft_logits.to(dev) if mode == SOFT else None, 1.0, mode, 8, ws)
+        torch.cuda.synchronize()
+        s = out.len_marginal.cpu().numpy().sum(axis=1)
+        say(f"  mode {mode}: |sum P(k) - 1| max {np.abs(s - 1).max():.2e}")
+        assert np.all(np.abs(s - 1.0) < 1e-12)
+
+
 # ---- scoring -----------------------------------------------------------------------------------
 @pytest.mark.parametrize("mode", [SOFT, POINT])
 @pytest.mark.parametrize("T", [1.0, 0.0])
