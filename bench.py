@@ -7,6 +7,8 @@ resident in HBM before the timed region.  Prints one JSON line.
 
   python bench.py [--steps 50] [--warmup 5] [--config qwen8b_k16] [--no-cpu-baseline]
   python bench.py --copy-probe     # plain device copy of known size (counter calibration)
+  python bench.py --next-rows      # latencies of anchor replacement, cache lookup,
+                                   # calibrated lengths and the geometric fan-out
   python bench.py --pmc-summary DIR
       turn four rocprofv3 counter runs under DIR (bench_FETCH_SIZE, bench_WRITE_SIZE,
       copy_FETCH_SIZE, copy_WRITE_SIZE, each holding run_counter_collection.csv) into
@@ -120,6 +122,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR")
+    ap.add_argument("--next-rows", action="store_true")
     args = ap.parse_args()
     if args.pmc_summary:
         return pmc_summary(args.pmc_summary, args.config)
@@ -134,6 +137,8 @@ def main():
 
     if args.copy_probe:
         return copy_probe(torch)
+    if args.next_rows:
+        return next_rows(torch, args)
 
     import draft_block_verification_rmsnorm_amd as jsv
     import synth
@@ -247,6 +252,61 @@ def cpu_baseline(cfg, head_cpu, blk, T, mode):
             "cores": threads, "kind": "oracle",
             "sample": f"{len(times)} whole verification calls of the benchmark block (float64 NumPy), "
                       f"median {sec:.2f} s per call"}
+
+
+def _event_median(torch, fn, n=50, warm=5):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return times[len(times) // 2]
+
+
+def next_rows(torch, args):
+    """Latency of the next-row calls on the benchmark shape: anchor replacement on predicted
+    states (one HBM stream over W, like verification), the cache hit test against a top-8
+    list, the calibrated length score and the host fan-out (K = 16, cache of 16)."""
+    import draft_block_verification_rmsnorm_amd as jsv
+    import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    head_cpu = synth.head_for(cfg)
+    blk = synth.make_block(head_cpu, cfg.batch, cfg.K, cfg.sigma, 1.0, seed=0)
+    head = jsv.LMHead(head_cpu.weight.to(dev), head_cpu.norm_weight.to(dev), cfg.eps)
+    hp = synth.predicted_hidden(blk.hidden, seed=0).to(dev)
+    drafts = blk.draft_tokens.to(dev)
+    G = blk.draft_logits.to(dev)
+    ws = jsv.new_workspace(head, cfg.batch, cfg.K, 8)
+    aout = jsv.AnchorOut(cfg.batch, dev)
+    t_anchor = _event_median(torch, lambda: jsv.anchor_replace(head, hp, drafts, ws, out=aout), n=20)
+    sc = jsv.score_outcomes(head, hp, drafts, G, 1.0, jsv.PROPOSAL_SOFTMAX, 8, ws)
+    vo = jsv.verify_block(head, blk.hidden.to(dev), drafts, G, 1.0, jsv.PROPOSAL_SOFTMAX, 1, 0, ws)
+    hit = torch.empty(cfg.batch, dtype=torch.int32, device=dev)
+    t_lookup = _event_median(torch, lambda: jsv.cache_lookup(vo.n_accepted, vo.committed, sc.out_len,
+                                                             sc.out_token, hit_index=hit))
+    pt = torch.rand(cfg.batch, cfg.K, dtype=torch.float64, device=dev)
+    lo = torch.empty(cfg.batch, cfg.K + 1, dtype=torch.float64, device=dev)
+    lf = torch.empty(cfg.batch, dtype=torch.int32, device=dev)
+    t_len = _event_median(torch, lambda: jsv.calibrated_lengths(pt, out=lo, flags=lf))
+    t0 = time.perf_counter()
+    for _ in range(1000):
+        jsv.geometric_fanout(0.89, 1.0, cfg.K, 16)
+    t_fan = (time.perf_counter() - t0) / 1000
+    abytes = algorithmic_bytes(cfg, 0.0, False)
+    print(json.dumps({"metric": "next-row call latency", "config": {"workload": cfg.name},
+                      "anchor_replace_ms": round(t_anchor, 4),
+                      "anchor_replace_hbm_frac": round(abytes / (t_anchor * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "cache_lookup_us": round(t_lookup * 1e3, 2),
+                      "calibrated_lengths_us": round(t_len * 1e3, 2),
+                      "geometric_fanout_host_us": round(t_fan * 1e6, 2)}), flush=True)
 
 
 def copy_probe(torch):

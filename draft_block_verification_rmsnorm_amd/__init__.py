@@ -5,6 +5,7 @@ The work happens in libjsverify.so (HIP kernels for gfx950, C ABI in
 include/jsverify.h); `jsverify` is its thin ctypes binding.
 """
 from .jsverify import (FLAG_ACCEPT_TIE, FLAG_CDF_TIE, FLAG_INVALID, FLAG_LOGIT_GAP,  # noqa: F401
-                       FLAG_TOPN_TIE, FLAG_ZERO_RESIDUAL, PROPOSAL_POINT, PROPOSAL_SOFTMAX, LMHead,
-                       ScoreOut, VerifyOut, lmhead_logits, load_library, new_workspace,
-                       score_outcomes, verify_block, verify_sample, verify_stats, workspace_bytes)
+                       FLAG_TOPN_TIE, FLAG_ZERO_RESIDUAL, PROPOSAL_POINT, PROPOSAL_SOFTMAX, AnchorOut,
+                       LMHead, ScoreOut, VerifyOut, anchor_replace, cache_lookup, calibrated_lengths,
+                       geometric_fanout, lmhead_logits, load_library, new_workspace, score_outcomes,
+                       verify_block, verify_sample, verify_stats, workspace_bytes)

@@ -311,4 +311,118 @@ jsv_status jsv_score_outcomes(const jsv_lm_head* head, const void* hidden_pred,
   return launch_score(a, stream) == hipSuccess ? JSV_OK : JSV_EHIP;
 }
 
+jsv_status jsv_anchor_replace(const jsv_lm_head* head, const void* hidden_pred,
+                              const int32_t* draft_tokens, int32_t B, int32_t K,
+                              int32_t* position, int32_t* token, uint32_t* flags, void* ws,
+                              size_t ws_bytes, void* hip_stream) {
+  int nks = 0;
+  jsv_status st = check_head(head, &nks);
+  if (st != JSV_OK) return st;
+  st = check_block(B, K, 0.f, JSV_PROPOSAL_POINT);
+  if (st != JSV_OK) return st;
+  if (hidden_pred == nullptr || !aligned16(hidden_pred) || draft_tokens == nullptr ||
+      position == nullptr || token == nullptr || ws == nullptr || !aligned16(ws))
+    return JSV_EINVAL;
+  if (ws_bytes < needed_bytes(head->vocab, B, K, 0, true)) return JSV_EWORKSPACE;
+  (void)hipGetLastError();
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const WsLayout L = ws_layout(head->vocab, B, K, 0);
+  char* w = static_cast<char*>(ws);
+  st = run_stats(head, nks, hidden_pred, B * (K + 1), reinterpret_cast<float*>(w + L.logits),
+                 nullptr, B, K, 0.f, JSV_PROPOSAL_POINT, 1, reinterpret_cast<RowStat*>(w + L.partial),
+                 reinterpret_cast<float*>(w + L.rnorm), stream);
+  if (st != JSV_OK) return st;
+  FinalArgs f = final_args(head, hidden_pred, draft_tokens, nullptr, B, K, 0.f, JSV_PROPOSAL_POINT,
+                           kFinalizeAnchor, w, L);
+  f.n_accepted = position;
+  f.committed = token;
+  f.flags = flags;
+  if (f.P <= 0 || launch_rowstat(f, stream) != hipSuccess || launch_scan(f, stream) != hipSuccess)
+    return JSV_EHIP;
+  return JSV_OK;
+}
+
+jsv_status jsv_cache_lookup(const int32_t* n_accepted, const int32_t* committed, int32_t B,
+                            int32_t K, const int32_t* out_len, const int32_t* out_token,
+                            int32_t top_n, int32_t* hit_index, void* hip_stream) {
+  if (B < 1 || B > 65535 || K < 1 || K > kMaxK || top_n < 1 || top_n > kMaxTopN) return JSV_EINVAL;
+  if (!n_accepted || !committed || !out_len || !out_token || !hit_index) return JSV_EINVAL;
+  (void)hipGetLastError();
+  return launch_lookup(n_accepted, committed, B, K, out_len, out_token, top_n, hit_index,
+                       static_cast<hipStream_t>(hip_stream)) == hipSuccess ? JSV_OK : JSV_EHIP;
+}
+
+jsv_status jsv_calibrated_lengths(const double* p_tilde, int32_t B, int32_t K, double* len_score,
+                                  uint32_t* flags, void* hip_stream) {
+  if (B < 1 || B > 65535 || K < 1 || K > kMaxK || p_tilde == nullptr || len_score == nullptr)
+    return JSV_EINVAL;
+  (void)hipGetLastError();
+  return launch_lengths(p_tilde, B, K, len_score, flags, static_cast<hipStream_t>(hip_stream)) ==
+                 hipSuccess ? JSV_OK : JSV_EHIP;
+}
+
+// Host computation: the candidates of the surrogate problem are the M most likely lengths
+// for M = 1..gamma+1 (paper App. F.2, proof of Proposition 2(a)).
+jsv_status jsv_geometric_fanout(double alpha, double rho, int32_t gamma, int32_t B,
+                                double* F_real, int32_t* F_int, double* hit_mass) {
+  if (!(alpha > 0.0 && alpha < 1.0) || !(rho > 0.0) || gamma < 1 || gamma > 64 || B < 2 ||
+      B > 1000000 || F_real == nullptr || F_int == nullptr)
+    return JSV_EINVAL;
+  const int n = gamma + 1;
+  double P[65], w[65], bestF[65];
+  int order[65];
+  for (int k = 0; k < n; ++k) {
+    P[k] = (k < gamma) ? pow(alpha, k) * (1.0 - alpha) : pow(alpha, gamma);
+    w[k] = pow(P[k], 1.0 / (1.0 + rho));
+    order[k] = k;
+  }
+  // lengths by P descending, ties to the lower k (insertion sort: n <= 65)
+  for (int i = 1; i < n; ++i) {
+    const int x = order[i];
+    int j = i - 1;
+    while (j >= 0 && (P[order[j]] < P[x] || (P[order[j]] == P[x] && order[j] > x))) {
+      order[j + 1] = order[j];
+      --j;
+    }
+    order[j + 1] = x;
+  }
+  double best = -1.0;
+  for (int M = 1; M <= n; ++M) {
+    double F[65] = {0.0}, ws = 0.0;
+    for (int i = 0; i < M; ++i) ws += w[order[i]];
+    bool feasible = true;
+    for (int i = 0; i < M; ++i) {
+      const int k = order[i];
+      F[k] = double(B) * w[k] / ws;
+      if (F[k] < 1.0) feasible = false;
+    }
+    if (!feasible) continue;
+    double obj = 0.0;
+    for (int k = 0; k < n; ++k)
+      if (F[k] >= 1.0) obj += P[k] * (1.0 - pow(F[k], -rho));
+    if (obj > best) {
+      best = obj;
+      memcpy(bestF, F, sizeof(double) * n);
+    }
+  }
+  if (best < 0.0) return JSV_EINVAL;  // unreachable for B >= 2: M = 1 gives F = B
+  int total = 0;
+  double rem[65];
+  for (int k = 0; k < n; ++k) {
+    F_real[k] = bestF[k];
+    F_int[k] = int(floor(bestF[k]));
+    rem[k] = bestF[k] - F_int[k];
+    total += F_int[k];
+  }
+  for (int left = B - total; left > 0; --left) {  // largest remainders, ties to the lower k
+    int kb = -1;
+    for (int k = 0; k < n; ++k)
+      if (rem[k] >= 0.0 && (kb < 0 || rem[k] > rem[kb])) kb = k;
+    F_int[kb] += 1;
+    rem[kb] = -1.0;
+  }
+  if (hit_mass) *hit_mass = best;
+  return JSV_OK;
+}
+
 }  // extern "C"

@@ -149,7 +149,7 @@ inline StatsPlan plan_stats(int64_t V, int M, int cus) {
 }
 constexpr int kMaxPlanRows = 8 * kRowsPerPass;  // verification and scoring: B (K + 1) <= 264
 
-enum FinalizeKind { kFinalizeVerify = 1, kFinalizeScore = 2 };
+enum FinalizeKind { kFinalizeVerify = 1, kFinalizeScore = 2, kFinalizeAnchor = 3 };
 
 // Finalize, in two launches: per-row tasks (combine the partials of a row; the exact
 // logit of a draft row at its draft token) over a grid of one-wave workgroups, then per
@@ -173,8 +173,8 @@ struct FinalArgs {
   RowStat* rowstat;       // [M] combined statistics
   DraftLogit* dlog;       // [M] (rows < K of each request)
   const float* rnorm;
-  int* n_accepted;
-  int* committed;
+  int* n_accepted;         // verify: k; anchor replacement: the position
+  int* committed;          // verify: committed tokens; anchor replacement: the token [B]
   uint32_t* flags;        // may be null
   RowFinal* rowfinal;
   ReqState* req;
@@ -222,5 +222,9 @@ hipError_t launch_rowstat(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_scan(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
+hipError_t launch_lookup(const int* n_accepted, const int* committed, int B, int K, const int* out_len,
+                         const int* out_token, int top_n, int* hit, hipStream_t stream);
+hipError_t launch_lengths(const double* p, int B, int K, double* out, uint32_t* flags,
+                          hipStream_t stream);
 
 }  // namespace jsv

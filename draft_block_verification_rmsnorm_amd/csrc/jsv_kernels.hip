@@ -880,6 +880,11 @@ __global__ __launch_bounds__(kWave) void scan_kernel(FinalArgs a) {
   if (lane == 0) a.req[b] = rq;
   if (sc.bad) {
     if (a.kind == kFinalizeVerify) write_verify(a, b, sc, -1, 0u);
+    if (a.kind == kFinalizeAnchor && lane == 0) {
+      a.n_accepted[b] = -1;
+      a.committed[b] = -1;
+      if (a.flags) a.flags[b] = JSV_FLAG_INVALID;
+    }
     if (a.kind == kFinalizeScore) {
       if (lane < a.top_n) {
         a.out_len[b * a.top_n + lane] = -1;
@@ -907,6 +912,14 @@ __global__ __launch_bounds__(kWave) void scan_kernel(FinalArgs a) {
     rf.s = st.s; rf.sq = st.sq; rf.alpha = alpha; rf.A = A;
     rf.m = st.m; rf.top2 = st.top2; rf.mq = st.mq; rf.idx = st.idx; rf.flags = st.flags;
     a.rowfinal[row] = rf;
+  }
+  if (a.kind == kFinalizeAnchor) {  // greedy rule on decoder logits: position and token
+    if (lane == 0) {
+      a.n_accepted[b] = k;
+      a.committed[b] = bonus;
+      if (a.flags) a.flags[b] = sc.f;
+    }
+    return;
   }
   if (a.kind == kFinalizeVerify) {
     // T = 0: the bonus is the argmax of row k.  T > 0 verification draws it in the
@@ -1130,6 +1143,44 @@ __global__ __launch_bounds__(kWave) void locate_kernel(SampleArgs a) {
     f |= JSV_FLAG_CDF_TIE;
   }
   write_verify(a.f, b, sc, tok, sc.f | f);
+}
+
+// ------------------------------------------------------------------------------------
+// Cache hit test (paper §4.1): grid B, one wave; lane i compares cached entry i (and
+// i + 64 beyond) with the realised (k, a).
+__global__ __launch_bounds__(kWave) void lookup_kernel(const int* n_accepted, const int* committed,
+                                                       int K, const int* out_len, const int* out_token,
+                                                       int top_n, int* hit) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int k = n_accepted[b];
+  const int a = (k >= 0 && k <= K) ? committed[b * (K + 1) + k] : -1;
+  int found = -1;
+  for (int i0 = 0; i0 < top_n && found < 0; i0 += kWave) {
+    const int i = i0 + lane;
+    const bool m = k >= 0 && k <= K && i < top_n && out_len[b * top_n + i] == k &&
+                   out_token[b * top_n + i] == a;
+    const uint64_t mask = __ballot(m);
+    if (mask) found = i0 + __builtin_ctzll(mask);
+  }
+  if (lane == 0) hit[b] = found;
+}
+
+// Calibrated length score (paper App. B.1): grid B, one wave; lane k forms
+// G(k) = prod_{i<=k} p_i from the estimates read into scalar registers in order.
+__global__ __launch_bounds__(kWave) void lengths_kernel(const double* p, int K, double* out,
+                                                        uint32_t* flags) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const double pl = (lane < K) ? p[b * K + lane] : 1.0;
+  const bool bad = __ballot(lane < K && !(pl >= 0.0 && pl <= 1.0)) != 0;
+  double G = 1.0, Gn = 1.0;  // G(lane), G(lane + 1)
+  for (int i = 0; i < K; ++i) {
+    const double pi = readlane_d(pl, i);
+    if (i < lane) G *= pi;
+    if (i <= lane) Gn *= pi;
+  }
+  if (lane == K) Gn = 0.0;
+  if (lane <= K) out[b * (K + 1) + lane] = bad ? 0.0 : G - Gn;
+  if (lane == 0 && flags) flags[b] = bad ? uint32_t(JSV_FLAG_INVALID) : 0u;
 }
 
 // ------------------------------------------------------------------------------------
@@ -1367,6 +1418,19 @@ hipError_t launch_rowstat(const FinalArgs& a, hipStream_t stream) {
 
 hipError_t launch_scan(const FinalArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(scan_kernel, dim3(a.B), dim3(kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lookup(const int* n_accepted, const int* committed, int B, int K, const int* out_len,
+                         const int* out_token, int top_n, int* hit, hipStream_t stream) {
+  hipLaunchKernelGGL(lookup_kernel, dim3(B), dim3(kWave), 0, stream, n_accepted, committed, K,
+                     out_len, out_token, top_n, hit);
+  return hipGetLastError();
+}
+
+hipError_t launch_lengths(const double* p, int B, int K, double* out, uint32_t* flags,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(lengths_kernel, dim3(B), dim3(kWave), 0, stream, p, K, out, flags);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ FLAG_ZERO_RESIDUAL = 1 << 4
 FLAG_TOPN_TIE = 1 << 5
 
 EXPORTED = ("jsv_workspace_bytes", "jsv_lmhead_logits", "jsv_verify_block", "jsv_verify_stats",
-            "jsv_verify_sample", "jsv_score_outcomes", "jsv_status_string", "jsv_version")
+            "jsv_verify_sample", "jsv_score_outcomes", "jsv_anchor_replace", "jsv_cache_lookup",
+            "jsv_calibrated_lengths", "jsv_geometric_fanout", "jsv_status_string", "jsv_version")
 
 _DTYPES = {torch.bfloat16: JSV_BF16, torch.float32: JSV_F32}
 
@@ -68,6 +69,16 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.jsv_score_outcomes.argtypes = [hp, vp, vp, vp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp,
                                        vp, sz, vp]
     lib.jsv_score_outcomes.restype = i32
+    lib.jsv_anchor_replace.argtypes = [hp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.jsv_anchor_replace.restype = i32
+    lib.jsv_cache_lookup.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp]
+    lib.jsv_cache_lookup.restype = i32
+    lib.jsv_calibrated_lengths.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.jsv_calibrated_lengths.restype = i32
+    f64 = ctypes.c_double
+    lib.jsv_geometric_fanout.argtypes = [f64, f64, i32, i32, ctypes.POINTER(f64), ctypes.POINTER(i32),
+                                         ctypes.POINTER(f64)]
+    lib.jsv_geometric_fanout.restype = i32
     lib.jsv_status_string.argtypes = [i32]
     lib.jsv_status_string.restype = ctypes.c_char_p
     lib.jsv_version.argtypes = []
@@ -235,3 +246,75 @@ def score_outcomes(head, hidden_pred, draft_tokens, draft_logits, temperature, m
         _ptr(out.out_prob), _ptr(out.len_marginal), _ptr(out.flags), _ptr(workspace),
         workspace.numel(), _stream(stream)))
     return out
+
+
+class AnchorOut:
+    def __init__(self, B, device):
+        self.position = torch.empty(B, dtype=torch.int32, device=device)
+        self.token = torch.empty(B, dtype=torch.int32, device=device)
+        self.flags = torch.empty(B, dtype=torch.int32, device=device)
+
+
+def anchor_replace(head, hidden_pred, draft_tokens, workspace, out=None, stream=None) -> AnchorOut:
+    """jsv_anchor_replace: first position whose decoder argmax differs from the draft, and
+    that token (K and the argmax of row K when every draft matches)."""
+    B, K = _block_checks(head, hidden_pred, draft_tokens, None, PROPOSAL_POINT, 0.0)
+    _need(workspace, "workspace", torch.uint8, device=head.device)
+    if out is None:
+        out = AnchorOut(B, head.device)
+    _check(load_library().jsv_anchor_replace(
+        ctypes.byref(head._c), _ptr(hidden_pred), _ptr(draft_tokens), B, K, _ptr(out.position),
+        _ptr(out.token), _ptr(out.flags), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def cache_lookup(n_accepted, committed, out_len, out_token, hit_index=None, stream=None):
+    """jsv_cache_lookup: index of the realised (k, a) in the cached top-N list, or -1."""
+    dev = n_accepted.device
+    B = n_accepted.shape[0]
+    _need(n_accepted, "n_accepted", torch.int32, (B,), dev)
+    if committed.dim() != 2 or committed.shape[0] != B:
+        raise ValueError("committed must be [B, K+1]")
+    K = committed.shape[1] - 1
+    _need(committed, "committed", torch.int32, (B, K + 1), dev)
+    if out_len.dim() != 2 or out_len.shape[0] != B:
+        raise ValueError("out_len must be [B, top_n]")
+    top_n = out_len.shape[1]
+    _need(out_len, "out_len", torch.int32, (B, top_n), dev)
+    _need(out_token, "out_token", torch.int32, (B, top_n), dev)
+    if hit_index is None:
+        hit_index = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(hit_index, "hit_index", torch.int32, (B,), dev)
+    _check(load_library().jsv_cache_lookup(_ptr(n_accepted), _ptr(committed), B, K, _ptr(out_len),
+                                           _ptr(out_token), top_n, _ptr(hit_index), _stream(stream)))
+    return hit_index
+
+
+def calibrated_lengths(p_tilde, out=None, flags=None, stream=None):
+    """jsv_calibrated_lengths: G(k) - G(k+1) from per-position estimates p_tilde [B, K]."""
+    if p_tilde.dim() != 2:
+        raise ValueError("p_tilde must be [B, K]")
+    B, K = p_tilde.shape
+    dev = p_tilde.device
+    _need(p_tilde, "p_tilde", torch.float64, (B, K), dev)
+    if out is None:
+        out = torch.empty(B, K + 1, dtype=torch.float64, device=dev)
+    if flags is None:
+        flags = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(out, "out", torch.float64, (B, K + 1), dev)
+    _need(flags, "flags", torch.int32, (B,), dev)
+    _check(load_library().jsv_calibrated_lengths(_ptr(p_tilde), B, K, _ptr(out), _ptr(flags),
+                                                 _stream(stream)))
+    return out, flags
+
+
+def geometric_fanout(alpha: float, rho: float, gamma: int, B: int):
+    """jsv_geometric_fanout (host): (F_real list, F_int list, hit mass)."""
+    fr = (ctypes.c_double * (gamma + 1))()
+    fi = (ctypes.c_int32 * (gamma + 1))()
+    hm = ctypes.c_double()
+    if not (1 <= gamma <= 64):
+        raise ValueError("gamma must be in 1..64")
+    _check(load_library().jsv_geometric_fanout(float(alpha), float(rho), int(gamma), int(B), fr, fi,
+                                               ctypes.byref(hm)))
+    return list(fr), list(fi), hm.value

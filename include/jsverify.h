@@ -151,6 +151,53 @@ jsv_status jsv_score_outcomes(const jsv_lm_head* head, const void* hidden_pred,
                               float* out_prob, double* len_marginal, uint32_t* flags,
                               void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Anchor replacement (paper §4.3 "Anchor Replacement"): the decoder reads predicted states
+   of the block and finds the first position whose most likely token differs from the
+   draft; its token is the replacement.  This is the greedy (T = 0) rule applied to the
+   decoder's logits.
+   hidden_pred:  device [B][K+1][hidden], `dtype`
+   draft_tokens: device [B][K] int32
+   Outputs (device): position [B] (first i < K with argmax z_i != d_i, or K when every
+   draft matches; -1 for an invalid request), token [B] (the argmax of that row, lowest
+   id on ties), flags [B] or NULL (JSV_FLAG_LOGIT_GAP, JSV_FLAG_INVALID).
+   Needs jsv_workspace_bytes(head, B, K, 0) of workspace. */
+jsv_status jsv_anchor_replace(const jsv_lm_head* head, const void* hidden_pred,
+                              const int32_t* draft_tokens, int32_t B, int32_t K,
+                              int32_t* position, int32_t* token, uint32_t* flags, void* ws,
+                              size_t ws_bytes, void* hip_stream);
+
+/* Cache hit test (paper §4.1): the realised outcome of request b is (k, a) with
+   k = n_accepted[b] and a = committed[b][k]; it hits when some entry i of the cached
+   list (out_len[b][i], out_token[b][i]) equals it.
+   n_accepted [B], committed [B][K+1] (as written by jsv_verify_block), out_len and
+   out_token [B][top_n] (as written by jsv_score_outcomes): device int32.
+   Output: hit_index [B] (device int32), the first matching entry, or -1 for a miss or
+   an invalid round (k < 0).  1 <= top_n <= 64, 1 <= K <= 32, B >= 1. */
+jsv_status jsv_cache_lookup(const int32_t* n_accepted, const int32_t* committed, int32_t B,
+                            int32_t K, const int32_t* out_len, const int32_t* out_token,
+                            int32_t top_n, int32_t* hit_index, void* hip_stream);
+
+/* Calibrated length score (paper App. B.1, Eq. 12): from per-position acceptance estimates
+   p_tilde[b][i] in [0, 1] of the 1-based positions i = 1..K, G(k) = prod_{i <= k} p_tilde_i
+   (G(0) = 1, G(K+1) = 0) and len_score[b][k] = G(k) - G(k+1), k = 0..K, in float64.
+   p_tilde: device [B][K] double; len_score: device [B][K+1] double; flags [B] or NULL.
+   A request with an estimate outside [0, 1] or not a number is flagged JSV_FLAG_INVALID
+   and scored 0.  1 <= K <= 32, B >= 1. */
+jsv_status jsv_calibrated_lengths(const double* p_tilde, int32_t B, int32_t K, double* len_score,
+                                  uint32_t* flags, void* hip_stream);
+
+/* SSD's geometric fan-out (paper App. F.2, Proposition 2(a)): anchors per accepted length
+   k = 0..gamma under the length law P(k) = alpha^k (1 - alpha) (k < gamma), alpha^gamma
+   (k = gamma), and the surrogate hit curve 1 - F^-rho, for a cache of B anchors.  The
+   active lengths are the M most likely ones (ties to the lower k) for the M whose series
+   F_k = B P(k)^(1/(1+rho)) / sum_active P^(1/(1+rho)) keeps every active F_k >= 1 and
+   captures the most hit mass sum_k P(k) (1 - F_k^-rho).  F_int rounds F_real down and
+   gives the remaining anchors to the largest remainders (ties to the lower k).
+   Host call (no device work): F_real [gamma+1] double, F_int [gamma+1] int32, hit_mass
+   (may be NULL).  0 < alpha < 1, rho > 0, 1 <= gamma <= 64, 2 <= B <= 1e6. */
+jsv_status jsv_geometric_fanout(double alpha, double rho, int32_t gamma, int32_t B,
+                                double* F_real, int32_t* F_int, double* hit_mass);
+
 /* Static text for a status code. */
 const char* jsv_status_string(jsv_status status);
 

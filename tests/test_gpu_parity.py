@@ -326,3 +326,86 @@ def test_stages_equal_block_and_runs_are_bit_identical(qwen, dev):
     assert torch.equal(outs[0][0].committed, o2.committed)
     assert torch.equal(outs[0][0].n_accepted, o2.n_accepted)
     assert torch.equal(outs[0][0].flags, o2.flags)
+
+
+# ---- next rows: anchor replacement, cache lookup, calibrated lengths ---------------------------
+def _compare_anchor(out, pos, tok, fl, st):
+    gp, gt, gf = (out.position.cpu().numpy(), out.token.cpu().numpy(), out.flags.cpu().numpy())
+    for b in range(pos.shape[0]):
+        st["requests"] += 1
+        assert (int(gf[b]) & oracle.FLAG_INVALID) == (int(fl[b]) & oracle.FLAG_INVALID)
+        if (int(gf[b]) | int(fl[b])) & oracle.FLAG_LOGIT_GAP:
+            st["near_ties"] += 1
+            continue
+        assert (int(gp[b]), int(gt[b])) == (int(pos[b]), int(tok[b])), (b, gp[b], gt[b], pos[b], tok[b])
+        st["exact"] += 1
+
+
+def test_anchor_replace_tiny_and_qwen(tiny, qwen, dev):
+    st = new_stats()
+    cfg = synth.CONFIGS["tiny"]
+    ws = jsv.new_workspace(tiny.gpu, 8, cfg.K)
+    for seed in range(40):
+        blk = synth.make_block(tiny.cpu, 8, cfg.K, cfg.sigma, 0.0, seed=900 + seed)
+        hp = synth.predicted_hidden(blk.hidden, seed=seed)
+        out = jsv.anchor_replace(tiny.gpu, hp.to(dev), blk.draft_tokens.to(dev), ws)
+        torch.cuda.synchronize()
+        _compare_anchor(out, *oracle.anchor_replace(tiny.oh, hp, blk.draft_tokens.numpy()), st)
+    for name in ("qwen8b_k16", "qwen8b_k32_b4"):
+        cfg = synth.CONFIGS[name]
+        ws = jsv.new_workspace(qwen.gpu, cfg.batch, cfg.K)
+        blk = synth.make_block(qwen.cpu, cfg.batch, cfg.K, cfg.sigma, 0.0, seed=77)
+        hp = synth.predicted_hidden(blk.hidden, seed=77)
+        say(f"anchor replacement {name}")
+        out = jsv.anchor_replace(qwen.gpu, hp.to(dev), blk.draft_tokens.to(dev), ws)
+        torch.cuda.synchronize()
+        _compare_anchor(out, *oracle.anchor_replace(qwen.oh, hp, blk.draft_tokens.numpy()), st)
+    say(f"  {st}")
+    assert st["exact"] >= 0.9 * st["requests"]
+
+
+def test_anchor_replace_invalid_draft(tiny, dev):
+    cfg = synth.CONFIGS["tiny"]
+    ws = jsv.new_workspace(tiny.gpu, 2, cfg.K)
+    blk = synth.make_block(tiny.cpu, 2, cfg.K, cfg.sigma, 0.0, seed=5)
+    d = blk.draft_tokens.clone()
+    d[1, 2] = cfg.vocab + 3
+    out = jsv.anchor_replace(tiny.gpu, blk.hidden.to(dev), d.to(dev), ws)
+    torch.cuda.synchronize()
+    pos, tok, fl = oracle.anchor_replace(tiny.oh, blk.hidden, d.numpy())
+    assert int(out.position[1]) == -1 and int(out.token[1]) == -1 and int(out.flags[1]) & jsv.FLAG_INVALID
+    assert int(out.position[0]) == int(pos[0]) or (int(fl[0]) | int(out.flags[0])) & jsv.FLAG_LOGIT_GAP
+
+
+def test_cache_lookup_matches_oracle(tiny, dev):
+    cfg = synth.CONFIGS["tiny"]
+    B, K, N = 8, cfg.K, 16
+    ws = jsv.new_workspace(tiny.gpu, B, K, N)
+    hits = 0
+    for seed in range(10):
+        blk = synth.make_block(tiny.cpu, B, K, cfg.sigma, 1.0, seed=1300 + seed)
+        hp = synth.predicted_hidden(blk.hidden, seed=seed)
+        dl = blk.draft_logits.to(dev)
+        sc = jsv.score_outcomes(tiny.gpu, hp.to(dev), blk.draft_tokens.to(dev), dl, 1.0, SOFT, N, ws)
+        vo = jsv.verify_block(tiny.gpu, blk.hidden.to(dev), blk.draft_tokens.to(dev), dl, 1.0, SOFT, seed, 0, ws)
+        hit = jsv.cache_lookup(vo.n_accepted, vo.committed, sc.out_len, sc.out_token)
+        torch.cuda.synchronize()
+        ref = oracle.cache_lookup(vo.n_accepted.cpu().numpy(), vo.committed.cpu().numpy(),
+                                  sc.out_len.cpu().numpy(), sc.out_token.cpu().numpy())
+        assert np.array_equal(hit.cpu().numpy(), ref)
+        hits += int((ref >= 0).sum())
+    say(f"  cache hits {hits} of {10 * B} rounds (top {N} of predicted states)")
+
+
+def test_calibrated_lengths_bit_exact(dev):
+    rng = np.random.default_rng(11)
+    for B, K in ((1, 1), (16, 16), (7, 32)):
+        p = rng.uniform(0.0, 1.0, size=(B, K))
+        if B > 2:
+            p[1, K // 2] = 1.5
+            p[2, 0] = np.nan
+        out, fl = jsv.calibrated_lengths(torch.tensor(p, dtype=torch.float64, device=dev))
+        torch.cuda.synchronize()
+        ref, rf = oracle.calibrated_lengths(p)
+        assert np.array_equal(out.cpu().numpy(), ref), (B, K)
+        assert np.array_equal(fl.cpu().numpy(), rf)

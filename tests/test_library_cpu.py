@@ -122,3 +122,39 @@ def test_lmhead_argument_errors(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         J.load_library(tmp_path / "libjsverify.so")
+
+
+def test_next_row_argument_errors(lib):
+    h = head()
+    st = lib.jsv_anchor_replace(ctypes.byref(h), FAKE, FAKE, 0, 16, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert st == J.JSV_EINVAL
+    st = lib.jsv_anchor_replace(ctypes.byref(h), FAKE, FAKE, 1, 16, None, FAKE, None, FAKE, 1 << 40, None)
+    assert st == J.JSV_EINVAL
+    st = lib.jsv_anchor_replace(ctypes.byref(h), FAKE, FAKE, 1, 16, FAKE, FAKE, None, FAKE, 10, None)
+    assert st == J.JSV_EWORKSPACE
+    assert lib.jsv_cache_lookup(FAKE, FAKE, 1, 16, FAKE, FAKE, 0, FAKE, None) == J.JSV_EINVAL
+    assert lib.jsv_cache_lookup(FAKE, FAKE, 1, 33, FAKE, FAKE, 8, FAKE, None) == J.JSV_EINVAL
+    assert lib.jsv_cache_lookup(None, FAKE, 1, 16, FAKE, FAKE, 8, FAKE, None) == J.JSV_EINVAL
+    assert lib.jsv_calibrated_lengths(FAKE, 1, 0, FAKE, None, None) == J.JSV_EINVAL
+    assert lib.jsv_calibrated_lengths(None, 1, 4, FAKE, None, None) == J.JSV_EINVAL
+
+
+def test_geometric_fanout_matches_oracle():
+    """The host fan-out is plain C in the library (no device work), so its parity with
+    the oracle is checked here, on the CPU."""
+    import numpy as np
+    import oracle
+    for alpha, rho, gamma, B in [(0.6, 1.0, 4, 10), (0.8, 0.5, 15, 16), (0.3, 2.0, 3, 6),
+                                 (0.93, 1.2, 31, 16), (0.5, 1.0, 6, 4), (0.99, 0.3, 64, 1000)]:
+        fr, fi, hm = J.geometric_fanout(alpha, rho, gamma, B)
+        F, Fi, obj, _ = oracle.geometric_fanout(alpha, rho, gamma, B)
+        assert np.allclose(fr, F, rtol=1e-12, atol=1e-12), (alpha, rho, gamma, B)
+        assert list(fi) == [int(x) for x in Fi], (alpha, rho, gamma, B)
+        assert abs(hm - obj) < 1e-12
+    fr, fi, hm = J.geometric_fanout(0.6, 1.0, 4, 10)
+    assert abs(hm - 0.567) < 5e-4 and fi == [3, 3, 2, 0, 2]
+    for bad in [(0.0, 1.0, 4, 10), (1.0, 1.0, 4, 10), (0.5, 0.0, 4, 10), (0.5, 1.0, 4, 1)]:
+        with pytest.raises(RuntimeError):
+            J.geometric_fanout(*bad)
+    with pytest.raises(ValueError):
+        J.geometric_fanout(0.5, 1.0, 0, 10)
