@@ -38,11 +38,14 @@ PEAK_BF16_TFLOPS = 2500.0
 
 
 def algorithmic_bytes(cfg, T, mode_softmax):
-    """Bytes the method must move per call: W once, hidden states, gamma, and the draft
-    logits when the softmax proposal needs q."""
-    esz = 2 if cfg.dtype == "bf16" else 4
+    """Bytes the method must move per call: W once (and its row scales for an fp8 head),
+    hidden states, gamma, and the draft logits when the softmax proposal needs q."""
+    wsz = {"bf16": 2, "f32": 4, "fp8": 1}[cfg.dtype]
+    xsz = 4 if cfg.dtype == "f32" else 2
     M = cfg.batch * (cfg.K + 1)
-    b = cfg.vocab * cfg.hidden * esz + M * cfg.hidden * esz + cfg.hidden * esz
+    b = cfg.vocab * cfg.hidden * wsz + M * cfg.hidden * xsz + cfg.hidden * xsz
+    if cfg.dtype == "fp8":
+        b += cfg.vocab * 4
     if mode_softmax and T > 0:
         b += cfg.batch * cfg.K * cfg.vocab * 4
     return b
@@ -150,7 +153,9 @@ def main():
     print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
     head_cpu = synth.head_for(cfg)
     blk = synth.make_block(head_cpu, cfg.batch, cfg.K, cfg.sigma, T, seed=0)
-    head = jsv.LMHead(head_cpu.weight.to(dev), head_cpu.norm_weight.to(dev), cfg.eps)
+    ws_ = head_cpu.weight_scale
+    head = jsv.LMHead(head_cpu.weight.to(dev), head_cpu.norm_weight.to(dev), cfg.eps,
+                      weight_scale=None if ws_ is None else ws_.to(dev))
     hidden = blk.hidden.to(dev)
     drafts = blk.draft_tokens.to(dev)
     G = blk.draft_logits.to(dev) if mode == jsv.PROPOSAL_SOFTMAX else None
@@ -239,7 +244,8 @@ def cpu_baseline(cfg, head_cpu, blk, T, mode):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    oh = oracle.Head(head_cpu.weight, head_cpu.norm_weight, cfg.eps, cfg.dtype)
+    oh = oracle.Head(head_cpu.weight, head_cpu.norm_weight, cfg.eps, cfg.dtype,
+                     weight_scale=head_cpu.weight_scale)
     dl = blk.draft_logits if mode == oracle.PROPOSAL_SOFTMAX else None
     times = []
     t_start = time.perf_counter()
@@ -280,7 +286,9 @@ def next_rows(torch, args):
     cfg = synth.CONFIGS[args.config]
     head_cpu = synth.head_for(cfg)
     blk = synth.make_block(head_cpu, cfg.batch, cfg.K, cfg.sigma, 1.0, seed=0)
-    head = jsv.LMHead(head_cpu.weight.to(dev), head_cpu.norm_weight.to(dev), cfg.eps)
+    ws_ = head_cpu.weight_scale
+    head = jsv.LMHead(head_cpu.weight.to(dev), head_cpu.norm_weight.to(dev), cfg.eps,
+                      weight_scale=None if ws_ is None else ws_.to(dev))
     hp = synth.predicted_hidden(blk.hidden, seed=0).to(dev)
     drafts = blk.draft_tokens.to(dev)
     G = blk.draft_logits.to(dev)

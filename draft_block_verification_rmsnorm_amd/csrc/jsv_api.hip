@@ -27,12 +27,17 @@ int device_cu_count() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int k_per_step(int dtype) { return dtype == JSV_BF16 ? 32 : 16; }
+int k_per_step(int dtype) { return dtype == JSV_F32 ? 16 : 32; }
+// Bytes per element of the hidden states and RMSNorm weight (bf16 for an fp8 head).
+size_t act_bytes(int dtype) { return dtype == JSV_F32 ? 4 : 2; }
 
 // Validates the head; on success *nks is hidden / (waves * k per MFMA step).
 jsv_status check_head(const jsv_lm_head* h, int* nks) {
   if (h == nullptr || h->weight == nullptr || h->norm_weight == nullptr) return JSV_EINVAL;
-  if (h->dtype != JSV_BF16 && h->dtype != JSV_F32) return JSV_EINVAL;
+  if (h->dtype != JSV_BF16 && h->dtype != JSV_F32 && h->dtype != JSV_FP8) return JSV_EINVAL;
+  if (h->dtype == JSV_FP8 && (h->weight_scale == nullptr ||
+                              (reinterpret_cast<uintptr_t>(h->weight_scale) & 3u) != 0))
+    return JSV_EINVAL;
   if (h->vocab < 1 || h->hidden < 1) return JSV_EINVAL;
   if (!(h->eps >= 0.f) || !isfinite(h->eps)) return JSV_EINVAL;
   if (!aligned16(h->weight) || !aligned16(h->norm_weight)) return JSV_EINVAL;
@@ -60,6 +65,7 @@ jsv_status run_stats(const jsv_lm_head* head, int nks, const void* hidden, int M
   if (cus <= 0) return JSV_EHIP;
   StatsArgs a{};
   a.W = head->weight;
+  a.wscale = head->dtype == JSV_FP8 ? head->weight_scale : nullptr;
   a.gamma = head->norm_weight;
   a.V = head->vocab;
   a.d = int(head->hidden);
@@ -74,7 +80,7 @@ jsv_status run_stats(const jsv_lm_head* head, int nks, const void* hidden, int M
   a.partial = partial;
   a.rnorm = rnorm;
   // Verification and scoring fit one launch; plain logits of many rows take several.
-  const size_t rowbytes = size_t(head->hidden) * (head->dtype == JSV_BF16 ? 2 : 4);
+  const size_t rowbytes = size_t(head->hidden) * act_bytes(head->dtype);
   for (int m0 = 0; m0 < M; m0 += kMaxPlanRows) {
     const int m = (M - m0) < kMaxPlanRows ? (M - m0) : kMaxPlanRows;
     if (stats && m0 > 0) return JSV_EUNSUPPORTED;
@@ -95,6 +101,7 @@ FinalArgs final_args(const jsv_lm_head* head, const void* hidden, const int32_t*
                      const WsLayout& L) {
   FinalArgs f{};
   f.W = head->weight;
+  f.wscale = head->dtype == JSV_FP8 ? head->weight_scale : nullptr;
   f.gamma = head->norm_weight;
   f.hidden = hidden;
   f.V = head->vocab;

@@ -114,6 +114,7 @@ inline WsLayout ws_layout(int64_t V, int B, int K, int top_n) {
 // the vocabulary into nchunk chunks.
 struct StatsArgs {
   const void* W;          // [V][d]
+  const float* wscale;    // [V] row scales of an fp8 head, else null
   const void* gamma;      // [d]
   const void* hidden;     // [M][d]
   int64_t V;
@@ -156,6 +157,7 @@ enum FinalizeKind { kFinalizeVerify = 1, kFinalizeScore = 2, kFinalizeAnchor = 3
 // request the acceptance scan (verify) or the outcome marginals (score).
 struct FinalArgs {
   const void* W;
+  const float* wscale;    // [V] row scales of an fp8 head, else null
   const void* gamma;
   const void* hidden;
   int64_t V;

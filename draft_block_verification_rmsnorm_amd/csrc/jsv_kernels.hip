@@ -174,6 +174,27 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 template <int DT> struct Elem;
 template <> struct Elem<JSV_BF16> { static constexpr int EPL = 8, ESZ = 2; };
 template <> struct Elem<JSV_F32> { static constexpr int EPL = 4, ESZ = 4; };
+// Element type of the hidden states, gamma and the normalised rows: an fp8 head keeps
+// them in bf16 (weight-only quantisation).
+template <int DT> struct Act { static constexpr int value = DT == JSV_FP8 ? JSV_BF16 : DT; };
+
+// W operand of MFMA k-step half h from a 16-byte W load: unchanged for bf16 and f32; for
+// an fp8 head the load holds 16 E4M3 codes, of which half h (8 codes) is widened to bf16
+// (exact: every E4M3 value is a bf16 value) with v_cvt_scalef32_pk_bf16_fp8.
+template <bool HI>
+__device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+template <int DT>
+__device__ inline uint4 wfrag(const uint4& f, int h) {
+  if constexpr (DT == JSV_FP8) {
+    const uint32_t w0 = h ? f.z : f.x, w1 = h ? f.w : f.y;
+    return make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                      fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+  } else {
+    return f;
+  }
+}
 
 template <int DT>
 __device__ inline void unpack(const uint4& q, float* x) {
@@ -399,8 +420,13 @@ constexpr int stage_groups(int NTOK) {
 // the 16 threads of a token merge their statistics into one partial.
 template <int DT, int NT, int NX, int NKS>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
-  constexpr int EPL = Elem<DT>::EPL, ESZ = Elem<DT>::ESZ, KS = 4 * EPL;
-  constexpr int D = pick_window(NT, NKS);
+  constexpr int XD = Act<DT>::value;                    // element type of h, gamma, x
+  constexpr int EPL = Elem<XD>::EPL, ESZ = Elem<XD>::ESZ, KS = 4 * EPL;
+  constexpr int SPL = DT == JSV_FP8 ? 2 : 1;            // MFMA k-steps per 16-byte W load
+  constexpr int WSZ = DT == JSV_FP8 ? 1 : ESZ;          // bytes per W element
+  constexpr int NL = NKS / SPL;                         // W loads per group and lane
+  constexpr int D = DT == JSV_FP8 ? NL : pick_window(NT, NKS);  // W loads in flight
+  static_assert(NL * SPL == NKS && NL >= 1, "fp8 needs an even number of k-steps");
   constexpr int NTOK = NT * 16 + NX;
   constexpr int NEP = (NTOK + 31) / 32;     // tokens per epilogue thread
   constexpr int XLEN = kWaves * NKS * 4;    // 16-byte groups per hidden row
@@ -440,15 +466,23 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   const int d = a.d;
   const int64_t r0 = V * wg / P, r1 = V * (wg + 1) / P;  // this workgroup's vocabulary rows
   const int ng = int((r1 - r0 + 15) >> 4);                // 16-row groups, the last may be partial
-  const int kb = w * (NKS * KS) + (lane >> 4) * EPL;
-  const uint32_t rowbytes = uint32_t(d) * ESZ;
+  const uint32_t rowbytes = uint32_t(d) * ESZ;   // hidden-state row
+  const uint32_t wrowbytes = uint32_t(d) * WSZ;  // W row
+  // Element offset in the row of the 8 (bf16) or 4 (f32) elements this lane feeds to
+  // MFMA k-step s; the W load u of the lane covers steps u*SPL .. u*SPL+SPL-1.
+  auto kofs = [&](int s) -> int {
+    if constexpr (DT == JSV_FP8)
+      return w * (NKS * KS) + (s >> 1) * (2 * KS) + (lane >> 4) * 16 + (s & 1) * 8;
+    else
+      return w * (NKS * KS) + s * KS + (lane >> 4) * EPL;
+  };
 
   // W rows [r0, r1) as one buffer; local group g of it at soffset 16 g rows.
-  const rsrc_t wr = make_rsrc(static_cast<const char*>(a.W) + (size_t)r0 * rowbytes,
-                              (uint64_t)(r1 - r0) * rowbytes);
-  const uint32_t wvoff = uint32_t(lane & 15) * rowbytes + uint32_t(kb) * ESZ;
-  auto wload = [&](int g, int s) -> uint4 {
-    return bload16(wr, wvoff + uint32_t(s * KS * ESZ), uint32_t(g) * 16u * rowbytes);
+  const rsrc_t wr = make_rsrc(static_cast<const char*>(a.W) + (size_t)r0 * wrowbytes,
+                              (uint64_t)(r1 - r0) * wrowbytes);
+  const uint32_t wvoff = uint32_t(lane & 15) * wrowbytes + uint32_t(kofs(0)) * WSZ;
+  auto wload = [&](int g, int u) -> uint4 {  // every load advances 64 bytes along the row
+    return bload16(wr, wvoff + uint32_t(u) * 64u, uint32_t(g) * 16u * wrowbytes);
   };
 
   // ---- RMSNorm of the rows of this pass ----------------------------------------------
@@ -473,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) xf[t][s] = bload16(hr, tokoff[t] + uint32_t(kb + s * KS) * ESZ, 0);
+    for (int s = 0; s < NKS; ++s) xf[t][s] = bload16(hr, tokoff[t] + uint32_t(kofs(s)) * ESZ, 0);
   uint4 xh[NX1][XPT];  // the VALU row, block-wide
 #pragma unroll
   for (int x = 0; x < NX; ++x)
@@ -498,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   for (int t = 0; t < NT; ++t) {
     double ps = 0.0;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) ps += sumsq16<DT>(xf[t][s]);
+    for (int s = 0; s < NKS; ++s) ps += sumsq16<XD>(xf[t][s]);
     ps = rows_sum(ps);
     if (lane < 16) ssq[w][t * 16 + lane] = ps;
   }
@@ -506,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   for (int x = 0; x < NX; ++x) {
     double ps = 0.0;
 #pragma unroll
-    for (int j = 0; j < XPT; ++j) ps += sumsq16<DT>(xh[x][j]);
+    for (int j = 0; j < XPT; ++j) ps += sumsq16<XD>(xh[x][j]);
     ps = wave_sum(ps);
     if (lane == 0) ssq[w][NT * 16 + x] = ps;
   }
@@ -536,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
       const int q = tid + j * kThreads;
-      if (q < XLEN) xrow[x][q] = norm_pack<DT>(xh[x][j], gsh[q], r);
+      if (q < XLEN) xrow[x][q] = norm_pack<XD>(xh[x][j], gsh[q], r);
     }
   }
   if (NX > 0) __syncthreads();
@@ -550,6 +584,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   const int qrow0 = a.want_q ? (row0 / (a.K + 1)) * a.K : 0;
   const int qrows = a.want_q ? ((row0 + rows - 1) / (a.K + 1)) * a.K + a.K - qrow0 : 0;
   const rsrc_t qr = make_rsrc(a.G + (size_t)qrow0 * V, (uint64_t)qrows * (uint64_t)V * 4u);
+  // Row scales of an fp8 head for this workgroup's rows.
+  const rsrc_t sr = make_rsrc(DT == JSV_FP8 ? a.wscale + r0 : a.logits,
+                              DT == JSV_FP8 ? uint64_t(r1 - r0) * 4u : 0u);
   int jj[NEP];
   bool tok_ok[NEP], qrow[NEP];
   uint32_t qoff[NEP];
@@ -577,6 +614,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     float gv[NEP];
 #pragma unroll
     for (int e = 0; e < NEP; ++e) gv[e] = bload4f(qr, qoff[e] + uint32_t(v) * 4u);
+    const float wsc = DT == JSV_FP8 ? bload4f(sr, uint32_t(g * 16 + ii) * 4u) : 1.f;
     floatx4 acc[NT1];
     float xacc[NX1];
 #pragma unroll
@@ -584,20 +622,25 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
     for (int x = 0; x < NX1; ++x) xacc[x] = 0.f;
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      if constexpr (FIRST) {
-        const uint4 gq = gsh[(kb + s * KS) / EPL];
+    for (int u = 0; u < NL; ++u) {
+      const uint4 fw = fr[u % D];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) xf[t][s] = norm_pack<DT>(xf[t][s], gq, rt[t]);
+      for (int h = 0; h < SPL; ++h) {
+        const int s = u * SPL + h;
+        if constexpr (FIRST) {
+          const uint4 gq = gsh[kofs(s) / EPL];
+#pragma unroll
+          for (int t = 0; t < NT; ++t) xf[t][s] = norm_pack<XD>(xf[t][s], gq, rt[t]);
+        }
+        const uint4 f = wfrag<DT>(fw, h);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma_step<XD>(f, xf[t][s], acc[t]);
+#pragma unroll
+        for (int x = 0; x < NX; ++x) xacc[x] = dot16<XD>(f, xrow[x][kofs(s) / EPL], xacc[x]);
       }
-      const uint4 f = fr[s % D];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = mfma_step<DT>(f, xf[t][s], acc[t]);
-#pragma unroll
-      for (int x = 0; x < NX; ++x) xacc[x] = dot16<DT>(f, xrow[x][(kb + s * KS) / EPL], xacc[x]);
-      // refill this slot D steps ahead (past the last group the loads read zeros)
-      const bool nxt = (s + D) >= NKS;
-      fr[s % D] = wload(nxt ? g + 1 : g, nxt ? (s + D - NKS) : (s + D));
+      // refill this slot D loads ahead (past the last group the loads read zeros)
+      const bool nxt = (u + D) >= NL;
+      fr[u % D] = wload(nxt ? g + 1 : g, nxt ? (u + D - NL) : (u + D));
     }
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
@@ -620,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
         for (int w2 = 0; w2 < kWaves; ++w2) zz += double(redx[buf][w2][x][ii]);
       }
-      const float z = float(zz);
+      const float z = DT == JSV_FP8 ? float(zz * double(wsc)) : float(zz);
       const bool valid = tok_ok[e] && vok;
       zst[jj[e]][(g - gb) * 16 + ii] = z;
       if (a.stats) {
@@ -715,6 +758,42 @@ __device__ double exact_logit(const FinalArgs& a, int row, int dt, float r) {
   return wave_sum(acc);
 }
 
+// The same for an fp8 head: W row dt holds E4M3 codes (one byte each) and a row scale;
+// h and gamma are bf16.  Each lane takes 16 consecutive elements per load of codes.
+__device__ double exact_logit_fp8(const FinalArgs& a, int row, int dt, float r) {
+  constexpr int NJ = 4;  // 16-code loads per lane per batch
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t wbytes = uint32_t(a.d), xbytes = uint32_t(a.d) * 2u;
+  const rsrc_t hr = make_rsrc(static_cast<const char*>(a.hidden) + (size_t)row * xbytes, xbytes);
+  const rsrc_t gr = make_rsrc(a.gamma, xbytes);
+  const rsrc_t wr = make_rsrc(static_cast<const char*>(a.W) + (size_t)dt * wbytes, wbytes);
+  double acc = 0.0;
+  for (uint32_t base = 0; base < wbytes; base += NJ * kWave * 16) {
+    uint4 wq[NJ], hq[2 * NJ], gq[2 * NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint32_t e0 = base + uint32_t(j * kWave + lane) * 16u;  // first element
+      wq[j] = bload16(wr, e0, 0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        hq[2 * j + h] = bload16(hr, (e0 + 8u * h) * 2u, 0);
+        gq[2 * j + h] = bload16(gr, (e0 + 8u * h) * 2u, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float xv[8], wv[8];
+        unpack<JSV_BF16>(norm_pack<JSV_BF16>(hq[2 * j + h], gq[2 * j + h], r), xv);
+        unpack<JSV_BF16>(wfrag<JSV_FP8>(wq[j], h), wv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fma(double(xv[e]), double(wv[e]), acc);
+      }
+  }
+  return wave_sum(acc) * double(a.wscale[dt]);
+}
+
 // Merge of the P partial records of one row, returned on every lane.
 __device__ Stat combine_row(const FinalArgs& a, int row, float c, bool soft) {
   const int lane = threadIdx.x & (kWave - 1), P = a.P;
@@ -763,7 +842,8 @@ __global__ __launch_bounds__(kWave) void rowstat_kernel(FinalArgs a) {
     if (dt >= 0 && (int64_t)dt < V) {
       if (a.mode == JSV_PROPOSAL_SOFTMAX) o.g = a.G[(size_t)(b * K + t) * V + dt];
       o.z = (a.dtype == JSV_BF16) ? exact_logit<JSV_BF16>(a, row, dt, r)
-                                  : exact_logit<JSV_F32>(a, row, dt, r);
+            : (a.dtype == JSV_FP8)  ? exact_logit_fp8(a, row, dt, r)
+                                    : exact_logit<JSV_F32>(a, row, dt, r);
     }
     if (lane == 0) a.dlog[row] = o;
   } else {
@@ -1371,7 +1451,8 @@ static hipError_t launch_stats_t(int grid, const StatsArgs& a, hipStream_t strea
 #define JSV_NKS_LIST(X) X(1) X(2) X(4) X(8) X(12) X(16) X(20)
 
 bool stats_supported(int dtype, int nks) {
-  if (dtype != JSV_BF16 && dtype != JSV_F32) return false;
+  if (dtype != JSV_BF16 && dtype != JSV_F32 && dtype != JSV_FP8) return false;
+  if (dtype == JSV_FP8 && (nks & 1)) return false;  // a 16-byte fp8 load spans two k-steps
   switch (nks) {
 #define JSV_CASE(n) case n: return true;
     JSV_NKS_LIST(JSV_CASE)
@@ -1383,7 +1464,10 @@ bool stats_supported(int dtype, int nks) {
 template <int DT, int NT, int NX>
 static hipError_t dispatch_nks(int nks, int grid, const StatsArgs& a, hipStream_t s) {
   switch (nks) {
-#define JSV_CASE(n) case n: return launch_stats_t<DT, NT, NX, n>(grid, a, s);
+#define JSV_CASE(n)                                                          \
+  case n:                                                                    \
+    if constexpr (DT == JSV_FP8 && (n & 1)) return hipErrorInvalidValue;   \
+    else return launch_stats_t<DT, NT, NX, n>(grid, a, s);
     JSV_NKS_LIST(JSV_CASE)
 #undef JSV_CASE
     default: return hipErrorInvalidValue;
@@ -1406,6 +1490,7 @@ hipError_t launch_stats(int dtype, int nks, int grid, const StatsArgs& a, hipStr
   if (a.rp < 1 || a.rp > kRowsPerPass || a.npass < 1 || a.nchunk < 1 || grid != a.nchunk * a.npass ||
       a.M > a.rp * a.npass)
     return hipErrorInvalidValue;
+  if (dtype == JSV_FP8) return dispatch_rows<JSV_FP8>(nks, grid, a, stream);
   return dtype == JSV_BF16 ? dispatch_rows<JSV_BF16>(nks, grid, a, stream)
                            : dispatch_rows<JSV_F32>(nks, grid, a, stream);
 }

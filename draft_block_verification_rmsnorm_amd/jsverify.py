@@ -16,7 +16,7 @@ import torch
 LIB_PATH = Path(__file__).resolve().parent / "libjsverify.so"
 
 JSV_OK, JSV_EINVAL, JSV_EUNSUPPORTED, JSV_EWORKSPACE, JSV_EHIP = 0, -1, -2, -3, -4
-JSV_BF16, JSV_F32 = 0, 1
+JSV_BF16, JSV_F32, JSV_FP8 = 0, 1, 2
 PROPOSAL_SOFTMAX, PROPOSAL_POINT = 0, 1
 
 FLAG_ACCEPT_TIE = 1 << 0
@@ -30,13 +30,13 @@ EXPORTED = ("jsv_workspace_bytes", "jsv_lmhead_logits", "jsv_verify_block", "jsv
             "jsv_verify_sample", "jsv_score_outcomes", "jsv_anchor_replace", "jsv_cache_lookup",
             "jsv_calibrated_lengths", "jsv_geometric_fanout", "jsv_status_string", "jsv_version")
 
-_DTYPES = {torch.bfloat16: JSV_BF16, torch.float32: JSV_F32}
+_DTYPES = {torch.bfloat16: JSV_BF16, torch.float32: JSV_F32, torch.float8_e4m3fn: JSV_FP8}
 
 
 class _Head(ctypes.Structure):
     _fields_ = [("weight", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
                 ("vocab", ctypes.c_int64), ("hidden", ctypes.c_int64),
-                ("eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("weight_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -119,18 +119,28 @@ def _need(t, name, dtype, shape=None, device=None):
 
 
 class LMHead:
-    """The target's final RMSNorm weight and LM-head weight, on one GPU."""
+    """The target's final RMSNorm weight and LM-head weight, on one GPU.
 
-    def __init__(self, weight: torch.Tensor, norm_weight: torch.Tensor, eps: float = 1e-6):
+    An fp8 head (weight in torch.float8_e4m3fn) takes `weight_scale`, one float32 scale
+    per vocabulary row, and a bfloat16 norm_weight; its hidden states are bfloat16."""
+
+    def __init__(self, weight: torch.Tensor, norm_weight: torch.Tensor, eps: float = 1e-6,
+                 weight_scale: torch.Tensor | None = None):
         if weight.dtype not in _DTYPES:
-            raise ValueError("weight must be bfloat16 or float32")
+            raise ValueError("weight must be bfloat16, float32 or float8_e4m3fn")
         _need(weight, "weight", weight.dtype)
-        _need(norm_weight, "norm_weight", weight.dtype, (weight.shape[1],), weight.device)
+        fp8 = weight.dtype == torch.float8_e4m3fn
+        self.act_dtype = torch.bfloat16 if fp8 else weight.dtype
+        _need(norm_weight, "norm_weight", self.act_dtype, (weight.shape[1],), weight.device)
+        if fp8:
+            _need(weight_scale, "weight_scale", torch.float32, (weight.shape[0],), weight.device)
         self.weight, self.norm_weight, self.eps = weight, norm_weight, float(eps)
+        self.weight_scale = weight_scale if fp8 else None
         self.dtype = weight.dtype
         self.vocab, self.hidden = int(weight.shape[0]), int(weight.shape[1])
         self._c = _Head(weight.data_ptr(), norm_weight.data_ptr(), self.vocab, self.hidden,
-                        self.eps, _DTYPES[weight.dtype])
+                        self.eps, _DTYPES[weight.dtype],
+                        weight_scale.data_ptr() if fp8 else None)
 
     @property
     def device(self):
@@ -151,7 +161,7 @@ def new_workspace(head: LMHead, batch: int, K: int, top_n: int = 0) -> torch.Ten
 
 def lmhead_logits(head: LMHead, hidden: torch.Tensor, out: torch.Tensor | None = None, stream=None):
     """RMSNorm + LM head of hidden [rows, d] -> fp32 logits [rows, V]."""
-    _need(hidden, "hidden", head.dtype, device=head.device)
+    _need(hidden, "hidden", head.act_dtype, device=head.device)
     if hidden.dim() != 2 or hidden.shape[1] != head.hidden:
         raise ValueError("hidden must be [rows, hidden]")
     rows = hidden.shape[0]
@@ -165,7 +175,7 @@ def lmhead_logits(head: LMHead, hidden: torch.Tensor, out: torch.Tensor | None =
 
 def _block_checks(head, hidden, draft_tokens, draft_logits, mode, temperature):
     if hidden is not None:
-        _need(hidden, "hidden", head.dtype, device=head.device)
+        _need(hidden, "hidden", head.act_dtype, device=head.device)
         if hidden.dim() != 3 or hidden.shape[2] != head.hidden:
             raise ValueError("hidden must be [B, K+1, hidden]")
         B, K = hidden.shape[0], hidden.shape[1] - 1

@@ -31,8 +31,9 @@
  *     hi32(seed)) and counter (row i, request b, lo32(offset), hi32(offset)); output
  *     word x0 gives u_i = x0 * 2^-32 for the acceptance test of row i, words x1, x2
  *     give v_i = (x1 * 2^21 + (x2 >> 11)) * 2^-53 for a bonus drawn at row i.
- *   - Supported shapes: hidden / 256 (bf16) or hidden / 128 (f32) in {1, 2, 4, 8, 12, 16, 20}
- *     (so d = 4096 and 5120 for bf16); 1 <= vocab <= 2^22; 1 <= K <= 32; 1 <= B <= 8.
+ *   - Supported shapes: hidden / 256 (bf16) or hidden / 128 (f32) in {1, 2, 4, 8, 12, 16, 20},
+ *     hidden / 256 in {2, 4, 8, 12, 16, 20} for fp8 (so d = 4096 and 5120 for bf16 and
+ *     fp8); 1 <= vocab <= 2^22; 1 <= K <= 32; 1 <= B <= 8.
  *     Anything else returns JSV_EUNSUPPORTED or JSV_EINVAL.
  */
 #ifndef JSVERIFY_H
@@ -53,7 +54,13 @@ typedef enum {
   JSV_EHIP = -4           /* the HIP runtime returned an error while enqueueing */
 } jsv_status;
 
-typedef enum { JSV_BF16 = 0, JSV_F32 = 1 } jsv_dtype;
+/* Element type of an LM head.  JSV_FP8 is a weight-only quantised head: `weight` holds OCP
+   FP8 E4M3 codes (one byte per element) and `weight_scale` one fp32 scale per vocabulary
+   row, W[v][j] = weight_scale[v] * e4m3(weight[v][j]); the RMSNorm weight and the hidden
+   states are bf16 and the normalised state is rounded to bf16, as for JSV_BF16.  Results
+   are exact with respect to that quantised head (paper App. F.3: the rule is lossless with
+   respect to the target it verifies against). */
+typedef enum { JSV_BF16 = 0, JSV_F32 = 1, JSV_FP8 = 2 } jsv_dtype;
 
 typedef enum {
   /* q_i = softmax(draft_logits_i / T); accept d_i with probability min(1, p_i(d_i)/q_i(d_i));
@@ -81,6 +88,7 @@ typedef struct {
   int64_t hidden;           /* d                                                               */
   float eps;                /* RMSNorm epsilon: x = gamma * h / sqrt(mean(h^2) + eps)          */
   int32_t dtype;            /* jsv_dtype of weight, norm_weight and hidden states             */
+  const float* weight_scale;/* device, [vocab] fp32 row scales for JSV_FP8; ignored otherwise  */
 } jsv_lm_head;
 
 /* Bytes of workspace any call with at most `batch` requests, `K` drafts and `top_n`

@@ -65,10 +65,14 @@ def bf16_round(x):
 
 
 def _as_f64(a):
-    """Any CPU array-like (NumPy, or a torch tensor of any float dtype) as float64 NumPy."""
+    """Any CPU array-like (NumPy, or a torch tensor of any float dtype, E4M3 codes
+    included) as float64 NumPy."""
     if hasattr(a, "detach"):
         import torch
-        return a.detach().to("cpu", torch.float64).numpy()
+        t = a.detach().to("cpu")
+        if t.dtype == torch.float8_e4m3fn:
+            t = t.to(torch.float32)   # every E4M3 value is a float32 value
+        return t.to(torch.float64).numpy()
     return np.asarray(a, dtype=np.float64)
 
 
@@ -309,13 +313,21 @@ def top_n(table, N):
 
 # ---- whole calls (the three library entry points) ---------------------------------------------
 class Head:
-    """LM head: weight [V, d], RMSNorm weight [d], epsilon and dtype ('bf16' | 'f32')."""
+    """LM head: weight [V, d], RMSNorm weight [d], epsilon and dtype ('bf16' | 'f32' |
+    'fp8').  An 'fp8' head holds E4M3 codes (a torch float8_e4m3fn tensor) and one scale
+    per vocabulary row, W[v] = weight_scale[v] * e4m3(code); its normalised state is
+    rounded to bf16 (weight-only quantisation; the verified target is the quantised one,
+    paper App. F.3 and §5 on the NVFP4 results)."""
 
-    def __init__(self, weight, norm_weight, eps, dtype):
+    def __init__(self, weight, norm_weight, eps, dtype, weight_scale=None):
         self.weight = weight
         self.norm_weight = norm_weight
         self.eps = float(np.float32(eps))
         self.dtype = dtype
+        self.act_dtype = "bf16" if dtype == "fp8" else dtype
+        self.weight_scale = None if weight_scale is None else _as_f64(weight_scale)
+        if dtype == "fp8" and self.weight_scale is None:
+            raise ValueError("an fp8 head needs row scales")
         self.vocab, self.hidden = int(weight.shape[0]), int(weight.shape[1])
 
 
@@ -323,8 +335,11 @@ def block_logits(head, hidden):
     """RMSNorm then LM head for rows [..., d] -> float64 logits [..., V]."""
     h = _as_f64(hidden)
     lead = h.shape[:-1]
-    xhat = rmsnorm(h.reshape(-1, head.hidden), head.norm_weight, head.eps, head.dtype)
-    return lm_head_logits(xhat, head.weight).reshape(*lead, head.vocab)
+    xhat = rmsnorm(h.reshape(-1, head.hidden), head.norm_weight, head.eps, head.act_dtype)
+    z = lm_head_logits(xhat, head.weight)
+    if head.weight_scale is not None:
+        z = z * head.weight_scale[None, :]
+    return z.reshape(*lead, head.vocab)
 
 
 def verify_block(head, hidden, draft_tokens, draft_logits, T, mode, seed, offset):

@@ -13,6 +13,9 @@ verification budgets 16 and 32 are reported):
   d_i    = argmax G_i at T = 0, else drawn from softmax(G_i / T)
   h_pred = h + N(0, 0.3^2)   (stand-in for adapter-predicted states, scoring only)
 W and gamma come from seed 1000 + config id; everything else from the run seed.
+An fp8 config quantises that bf16 W per vocabulary row: scale = max|W_v| / 448 (the
+largest E4M3 value), codes = E4M3(W_v / scale) rounded to nearest even; gamma and the
+hidden states stay bf16.  The quantised head is the target the verification runs on.
 """
 from __future__ import annotations
 
@@ -23,7 +26,9 @@ import torch
 
 BF16 = "bf16"
 F32 = "f32"
+FP8 = "fp8"
 _TORCH_DTYPE = {BF16: torch.bfloat16, F32: torch.float32}
+_ACT_DTYPE = {BF16: torch.bfloat16, F32: torch.float32, FP8: torch.bfloat16}
 
 # sigma of the draft perturbation, bisected at T = 0 so that the mean number of
 # committed tokens per block (accepted drafts + 1 bonus) is about 8 at K = 16 and
@@ -59,15 +64,25 @@ CONFIGS = {
                            SIGMA_K16_D5120, 1005),
     "d5120_k32_b2": Config("d=5120 V=151936 K=32 B=2 bf16", 151936, 5120, 32, 2, BF16, 0.02,
                            SIGMA_K32_D5120, 1005),
+    "qwen8b_k16_fp8": Config("Qwen3-8B LM head d=4096 V=151936 K=16 B=1 fp8 (E4M3 W, bf16 x)", 151936,
+                             4096, 16, 1, FP8, 0.02, SIGMA_K16_D4096, 1002),
 }
 
 
 @dataclass
 class HeadData:
-    weight: torch.Tensor        # [V, d] CPU, weight dtype
-    norm_weight: torch.Tensor   # [d]    CPU, weight dtype
+    weight: torch.Tensor        # [V, d] CPU, weight dtype (float8_e4m3fn codes for fp8)
+    norm_weight: torch.Tensor   # [d]    CPU, activation dtype
     eps: float
     dtype: str
+    weight_scale: torch.Tensor | None = None   # [V] float32 row scales of an fp8 head
+
+    def dequantized(self, v0=0, v1=None):
+        """Rows [v0, v1) of W as float32 values (codes times row scales for fp8)."""
+        w = self.weight[v0:v1].float()
+        if self.weight_scale is not None:
+            w = w * self.weight_scale[v0:v1, None]
+        return w
 
     @property
     def vocab(self):
@@ -119,7 +134,23 @@ def make_head(vocab, hidden, dtype, w_std, seed, eps=1e-6):
     return HeadData(w, gamma, float(eps), dtype)
 
 
+def quantize_fp8(head: HeadData) -> HeadData:
+    """Per-row E4M3 quantisation of a bf16 head (the fp8 workload recipe above)."""
+    w = head.weight.float()
+    amax = w.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).float()
+    codes = (w / scale[:, None]).to(torch.float8_e4m3fn)
+    return HeadData(codes, head.norm_weight.to(torch.bfloat16), head.eps, FP8, scale)
+
+
+@lru_cache(maxsize=2)
+def _fp8_head(vocab, hidden, w_std, seed, eps):
+    return quantize_fp8(make_head(vocab, hidden, BF16, w_std, seed, eps))
+
+
 def head_for(cfg: Config):
+    if cfg.dtype == FP8:
+        return _fp8_head(cfg.vocab, cfg.hidden, cfg.w_std, cfg.head_seed, cfg.eps)
     return make_head(cfg.vocab, cfg.hidden, cfg.dtype, cfg.w_std, cfg.head_seed, cfg.eps)
 
 
@@ -129,7 +160,7 @@ def draft_logits_for(head: HeadData, hidden_rows, chunk=16384):
                                      head.norm_weight.float(), head.eps)
     out = torch.empty(x.shape[0], head.vocab, dtype=torch.float32)
     for v0 in range(0, head.vocab, chunk):
-        wc = head.weight[v0:v0 + chunk].float()
+        wc = head.dequantized(v0, v0 + chunk)
         out[:, v0:v0 + wc.shape[0]] = x @ wc.T
     return out
 
@@ -137,7 +168,7 @@ def draft_logits_for(head: HeadData, hidden_rows, chunk=16384):
 def make_block(head: HeadData, batch, K, sigma, T, seed, hidden_std=1.0):
     """One verification block per request: target states, drafts and draft logits."""
     g = _gen(seed)
-    td = _TORCH_DTYPE[head.dtype]
+    td = _ACT_DTYPE[head.dtype]
     d, V = head.hidden, head.vocab
     h = (torch.randn(batch, K + 1, d, generator=g) * hidden_std).to(td)
     noise = torch.randn(batch, K, d, generator=g) * sigma
@@ -157,5 +188,7 @@ def predicted_hidden(hidden, seed, std=0.3):
 
 
 def random_head(vocab, hidden, dtype, seed, w_std=0.05, eps=1e-6):
-    """Small uncached head for tests (same recipe as make_head)."""
+    """Small uncached head for tests (same recipe as make_head; fp8 quantises it)."""
+    if dtype == FP8:
+        return quantize_fp8(make_head.__wrapped__(vocab, hidden, BF16, w_std, seed, eps))
     return make_head.__wrapped__(vocab, hidden, dtype, w_std, seed, eps)

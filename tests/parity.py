@@ -36,9 +36,11 @@ class Case:
     def __init__(self, head_cpu: synth.HeadData, dev, f64_weight=False):
         self.cpu = head_cpu
         self.dev = dev
-        self.gpu = jsv.LMHead(head_cpu.weight.to(dev), head_cpu.norm_weight.to(dev), head_cpu.eps)
-        w = head_cpu.weight.double().numpy() if f64_weight else head_cpu.weight
-        self.oh = oracle.Head(w, head_cpu.norm_weight, head_cpu.eps, head_cpu.dtype)
+        ws = head_cpu.weight_scale
+        self.gpu = jsv.LMHead(head_cpu.weight.to(dev), head_cpu.norm_weight.to(dev), head_cpu.eps,
+                              weight_scale=None if ws is None else ws.to(dev))
+        w = head_cpu.weight.float().double().numpy() if f64_weight else head_cpu.weight
+        self.oh = oracle.Head(w, head_cpu.norm_weight, head_cpu.eps, head_cpu.dtype, weight_scale=ws)
 
 
 def run_verify(case: Case, blk: synth.BlockData, T, mode, seed, offset, ws, with_logits=True):

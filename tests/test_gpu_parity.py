@@ -41,13 +41,14 @@ def qwen(dev):
 @pytest.mark.parametrize("V,d,dtype,rows", [
     (1024, 256, synth.F32, 5), (1000, 256, synth.BF16, 3), (4099, 512, synth.BF16, 17),
     (2048, 4096, synth.BF16, 40), (777, 5120, synth.BF16, 33), (300, 1024, synth.F32, 1),
+    (4099, 512, synth.FP8, 17), (1000, 5120, synth.FP8, 33),
 ])
 def test_lmhead_logits(dev, V, d, dtype, rows):
     say(f"lmhead V={V} d={d} {dtype} rows={rows}")
     head = synth.random_head(V, d, dtype, seed=V + d)
     case = Case(head, dev)
     g = torch.Generator().manual_seed(rows)
-    h = torch.randn(rows, d, generator=g).to(head.weight.dtype)
+    h = torch.randn(rows, d, generator=g).to(head.norm_weight.dtype)
     z = jsv.lmhead_logits(case.gpu, h.to(dev))
     torch.cuda.synchronize()
     ref = oracle.lmhead_logits(case.oh, h)
@@ -142,6 +143,24 @@ def test_cdf_drift_within_window(qwen, dev):
                 worst = max(worst, dr)
     say(f"  largest CDF drift {worst:.3e} (window {oracle.CDF_TIE:.0e})")
     assert worst < 0.5 * oracle.CDF_TIE
+
+
+def test_verify_qwen8b_fp8(dev):
+    """The fp8 (E4M3 weights, bf16 states) head at the Qwen3-8B shape: exact against the
+    oracle's quantised target."""
+    cfg = synth.CONFIGS["qwen8b_k16_fp8"]
+    case = Case(synth.head_for(cfg), dev, f64_weight=True)
+    ws = jsv.new_workspace(case.gpu, 1, cfg.K)
+    st = new_stats()
+    for T in (0.0, 1.0):
+        for seed in range(2):
+            say(f"qwen8b fp8 verify T={T} seed={seed}")
+            blk = synth.make_block(case.cpu, 1, cfg.K, cfg.sigma, T, seed=60 + seed)
+            got, ref = run_verify(case, blk, T, SOFT, seed, 3, ws)
+            compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+            compare_logits(got["logits"], ref["logits"], st)
+    say(f"  {st}")
+    assert st["exact"] >= 3
 
 
 def test_verify_qwen8b_k32_b4(qwen, dev):

@@ -158,3 +158,12 @@ def test_geometric_fanout_matches_oracle():
             J.geometric_fanout(*bad)
     with pytest.raises(ValueError):
         J.geometric_fanout(0.5, 1.0, 0, 10)
+
+
+def test_fp8_head_validation(lib):
+    ok = J._Head(FAKE, FAKE, 151936, 4096, 1e-6, J.JSV_FP8, FAKE)
+    assert lib.jsv_workspace_bytes(ctypes.byref(ok), 1, 16, 8) > 0
+    no_scale = J._Head(FAKE, FAKE, 151936, 4096, 1e-6, J.JSV_FP8, None)
+    assert lib.jsv_workspace_bytes(ctypes.byref(no_scale), 1, 16, 8) == 0
+    odd_steps = J._Head(FAKE, FAKE, 1024, 256, 1e-6, J.JSV_FP8, FAKE)   # one k-step per wave
+    assert lib.jsv_workspace_bytes(ctypes.byref(odd_steps), 1, 16, 8) == 0

@@ -89,3 +89,36 @@ def test_block_logits_pipeline_shapes():
     assert z.shape == (2, 3, 50)
     x = oracle.rmsnorm(h.reshape(6, 32), head.norm_weight, 1e-6, "bf16")
     assert np.allclose(z.reshape(6, 50), x @ head.weight.double().numpy().T)
+
+
+def test_e4m3_decode_matches_format_definition():
+    """OCP FP8 E4M3 (the fp8 head's codes): sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN and there are no
+    infinities.  The oracle decodes codes through torch; this pins that decoding to the
+    definition written out here, for all 256 codes."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    got = oracle.reference._as_f64(codes.view(torch.float8_e4m3fn))
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            assert np.isnan(got[c]), c
+            continue
+        val = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        assert got[c] == (-val if s else val), (c, got[c], val)
+
+
+def test_fp8_head_logits_closed_form():
+    """z = scale_v * (x . e4m3(code_v)) with x rounded to bf16: the same as the float64
+    product of x with the dequantised rows."""
+    rng = np.random.default_rng(5)
+    V, d = 64, 32
+    codes = torch.tensor(rng.normal(0, 30, size=(V, d)), dtype=torch.float32).to(torch.float8_e4m3fn)
+    scale = torch.tensor(rng.uniform(1e-4, 1e-3, size=V), dtype=torch.float32)
+    gamma = torch.tensor(1 + 0.01 * rng.normal(size=d), dtype=torch.float32).to(torch.bfloat16)
+    h = torch.tensor(rng.normal(size=(3, d)), dtype=torch.float32).to(torch.bfloat16)
+    head = oracle.Head(codes, gamma, 1e-6, "fp8", weight_scale=scale)
+    z = oracle.block_logits(head, h)
+    x = oracle.rmsnorm(h, gamma, 1e-6, "bf16")
+    wdq = codes.to(torch.float32).double().numpy() * scale.double().numpy()[:, None]
+    assert np.allclose(z, x @ wdq.T, rtol=1e-13, atol=1e-15)
+    assert np.all(oracle.bf16_round(x.astype(np.float32)) == x)  # x sits on the bf16 grid
