@@ -518,6 +518,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
                                         : kOutOfRange, 0);
     }
   asm volatile("" ::: "memory");  // keep the W loads behind the loads above
+  // Every wave's hidden-state requests go out before any wave's W requests: the compute
+  // unit's memory pipeline serves them in order, and the norm waits on the slowest wave.
+  __syncthreads();
   uint4 fr[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) fr[j] = wload(0, j);
