@@ -274,6 +274,45 @@ def test_score_qwen8b_k16(qwen, dev, mode):
     assert st["exact"] >= 1
 
 
+def test_score_k32_b4_d5120_fp8(qwen, dev):
+    """Scoring at the other shapes: K = 32 with B = 4 (four row passes), d = 5120, and the
+    fp8 head; top-8, T = 1, softmax proposal."""
+    st = new_stats()
+    cfg = synth.CONFIGS["qwen8b_k32_b4"]
+    ws = jsv.new_workspace(qwen.gpu, cfg.batch, cfg.K, 8)
+    blk = synth.make_block(qwen.cpu, cfg.batch, cfg.K, cfg.sigma, 1.0, seed=31)
+    say("score qwen8b K=32 B=4")
+    got, ref = run_score(qwen, synth.predicted_hidden(blk.hidden, 31), blk.draft_tokens,
+                         blk.draft_logits, 1.0, SOFT, 8, ws)
+    compare_score(got, ref, st)
+    for name in ("d5120_k16_b1", "qwen8b_k16_fp8"):
+        cfg = synth.CONFIGS[name]
+        case = Case(synth.head_for(cfg), dev, f64_weight=True)
+        ws = jsv.new_workspace(case.gpu, 1, cfg.K, 8)
+        blk = synth.make_block(case.cpu, 1, cfg.K, cfg.sigma, 1.0, seed=33)
+        say(f"score {name}")
+        got, ref = run_score(case, synth.predicted_hidden(blk.hidden, 33), blk.draft_tokens,
+                             blk.draft_logits, 1.0, SOFT, 8, ws)
+        compare_score(got, ref, st)
+        del case
+    say(f"  {st}")
+    assert st["exact"] >= 3
+
+
+def test_verify_qwen8b_k16_more_seeds(qwen, dev):
+    """Eight more seeds of the benchmark block at T = 1 (softmax proposal): exact except
+    at flagged near-ties."""
+    cfg = synth.CONFIGS["qwen8b_k16"]
+    ws = jsv.new_workspace(qwen.gpu, 1, cfg.K)
+    st = new_stats()
+    for seed in range(10, 18):
+        blk = synth.make_block(qwen.cpu, 1, cfg.K, cfg.sigma, 1.0, seed=seed)
+        got, ref = run_verify(qwen, blk, 1.0, SOFT, seed, seed, ws, with_logits=False)
+        compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+    say(f"  {st}")
+    assert st["exact"] >= 6
+
+
 # ---- edge cases ---------------------------------------------------------------------------------
 def test_edge_max_block_ragged_vocab(dev):
     # B = 8, K = 32: 264 rows in nine passes over a vocabulary that is not a multiple of 16
