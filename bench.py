@@ -131,8 +131,8 @@ def main():
         return pmc_summary(args.pmc_summary, args.config)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the verification call runs on one device; see DESIGN.md for how it would shard)",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(a verification call runs on one device)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -14,7 +14,7 @@ Notation: a request holds K draft tokens d_0..d_{K-1} and K+1 target rows.  Row
 i < K is the target distribution p_i that verifies d_i; row K is the distribution
 after the whole block ("position gamma+1" in the paper's 1-based notation).
 
-Readings of points the pages leave open (each is listed again in the design doc):
+Readings of points the pages leave open:
   * RMSNorm formula, epsilon and rounding points are not on the pages; the plain
     definition gamma * h / sqrt(mean(h^2) + eps) is used, computed in fp32 steps
     and rounded once to the weight dtype before the LM head.
