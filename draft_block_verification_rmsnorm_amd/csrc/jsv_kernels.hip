@@ -86,6 +86,51 @@ __device__ inline void bstore4f_nt(float x, rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, 0, 2);
 }
 
+// Loads from a buffer straight into LDS.  The lanes' data land lane-linearly at the LDS
+// byte address `lds` (wave-uniform), whatever addresses the lanes read; completion is
+// counted by vmcnt.  They are written as inline assembly on purpose: the compiler then
+// never sees LDS written by DMA, so it adds no wait-for-everything before each LDS read
+// or barrier, and the kernel waits for exactly the loads it needs (waits below).  The
+// descriptor is a raw buffer in SGPRs; the offset is range-checked (zeros past the end).
+struct Srd { u32x4 v; };
+__device__ inline Srd make_srd(const void* base, uint64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  Srd r;
+  r.v.x = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  r.v.y = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32) & 0xffffu);
+  r.v.z = __builtin_amdgcn_readfirstlane(bytes > 0xffffffffull ? 0xffffffffu : uint32_t(bytes));
+  r.v.w = uint32_t(kRsrcWord3);
+  return r;
+}
+__device__ inline uint32_t lds_addr(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_readfirstlane(
+      uint32_t(uintptr_t((const __attribute__((address_space(3))) char*)p)));
+#else
+  (void)p;
+  return 0;
+#endif
+}
+// m0 is listed as clobbered although the compiler reserves it: none of these kernels uses
+// m0 otherwise (gfx9 LDS instructions do not read it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane (1 KB per wave), non-temporal.
+__device__ inline void dma16_nt(Srd r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               ::"s"(lds), "v"(voff), "s"(r.v) : "memory", "m0");
+}
+// 4 bytes per lane (256 B per wave).
+__device__ inline void dma4(Srd r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               ::"s"(lds), "v"(voff), "s"(r.v) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Waits that also order the compiler's memory accesses around them.
+template <int N>
+__device__ inline void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ inline void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 __device__ inline double u2d(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(double, (uint64_t(hi) << 32) | uint64_t(lo));
 }
@@ -400,9 +445,12 @@ constexpr int pick_window(int NT, int NKS) {
 // ------------------------------------------------------------------------------------
 template <bool B> struct Tag { static constexpr bool value = B; };
 
-// Logit groups staged in LDS between write-outs (at most 96 KB of staging).
-constexpr int stage_groups(int NTOK) {
-  const int g = (96 * 1024) / (NTOK * 16 * 4);
+// Logit groups staged in LDS between write-outs: at most 96 KB of staging, and no more
+// than the LDS left over by the other arrays (`used` bytes of the 160 KB).
+constexpr int stage_groups(int NTOK, int used) {
+  const int room = 160 * 1024 - 512 - used;
+  const int budget = room < 96 * 1024 ? room : 96 * 1024;
+  const int g = budget / (NTOK * 16 * 4);
   return g > 64 ? 64 : g;
 }
 
@@ -427,12 +475,24 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   constexpr int NL = NKS / SPL;                         // W loads per group and lane
   constexpr int D = DT == JSV_FP8 ? NL : pick_window(NT, NKS);  // W loads in flight
   static_assert(NL * SPL == NKS && NL >= 1, "fp8 needs an even number of k-steps");
+  // bf16 with whole quarters (4 k-steps, 128 elements) in a wave's slice: W goes to LDS
+  // by DMA loads that each read 4 rows x 256 contiguous bytes, whole cache lines and
+  // non-temporal, RQ quarters ahead; the MFMA fragments are read back from LDS.
+  constexpr bool LDSW = DT == JSV_BF16 && NKS % 4 == 0;
+  constexpr int NQ = NKS / 4 > 0 ? NKS / 4 : 1;  // quarters per slice
+  constexpr int RQ = NT <= 1 ? 3 : 2;           // 4 KB quarter slots per wave
   constexpr int NTOK = NT * 16 + NX;
+  constexpr int NGI = (NTOK + 3) / 4;       // 256-byte DMA loads of a group's draft logits
   constexpr int NEP = (NTOK + 31) / 32;     // tokens per epilogue thread
   constexpr int XLEN = kWaves * NKS * 4;    // 16-byte groups per hidden row
   constexpr int XPT = (XLEN + kThreads - 1) / kThreads;
-  constexpr int SF = stage_groups(NTOK);
   constexpr int NT1 = NT > 0 ? NT : 1, NX1 = NX > 0 ? NX : 1;
+  constexpr int RING = LDSW ? kWaves * RQ * 256 : 1;  // uint4 entries
+  constexpr int SF = stage_groups(NTOK, 2 * kWaves * NT1 * kWave * 16 + 2 * kWaves * NX1 * 16 * 4 +
+                                            NX1 * XLEN * 16 + XLEN * 16 + kWaves * kRowsPerPass * 8 +
+                                            kRowsPerPass * 4 + 16 + RING * 16 +
+                                            (LDSW ? 2 * NGI * 4 * 16 * 4 : 64));
+  static_assert(SF >= 1, "LDS");
   static_assert(NTOK >= 1 && NTOK <= kRowsPerPass && NX <= 1, "tiling");
   __shared__ floatx4 red[2][kWaves][NT1][kWave];
   __shared__ float redx[2][kWaves][NX1][16];
@@ -441,6 +501,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   __shared__ float zst[NTOK][SF * 16];
   __shared__ double ssq[kWaves][kRowsPerPass];
   __shared__ float rnorm[kRowsPerPass];
+  __shared__ uint4 wring[RING];
+  __shared__ float gvs[LDSW ? 2 : 1][LDSW ? NGI * 4 : 1][16];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   // Workgroup -> (vocabulary chunk, pass of rows).  The passes of one chunk sit on the
@@ -477,12 +539,39 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       return w * (NKS * KS) + s * KS + (lane >> 4) * EPL;
   };
 
-  // W rows [r0, r1) as one buffer; local group g of it at soffset 16 g rows.
+  // W rows [r0, r1) as one buffer.  Every offset goes in the range-checked voffset (the
+  // soffset is not range-checked), so rows past r1 read as zero and cost no traffic.
   const rsrc_t wr = make_rsrc(static_cast<const char*>(a.W) + (size_t)r0 * wrowbytes,
                               (uint64_t)(r1 - r0) * wrowbytes);
   const uint32_t wvoff = uint32_t(lane & 15) * wrowbytes + uint32_t(kofs(0)) * WSZ;
   auto wload = [&](int g, int u) -> uint4 {  // every load advances 64 bytes along the row
-    return bload16(wr, wvoff + uint32_t(u) * 64u, uint32_t(g) * 16u * wrowbytes);
+    return bload16(wr, wvoff + uint32_t(g) * 16u * wrowbytes + uint32_t(u) * 64u, 0);
+  };
+  // LDS staging.  DMA instruction q of quarter c fills 1 KB of the wave's slot: lane p
+  // reads row 4q + p/16, 16-byte chunk k = (p mod 16) xor row of the quarter's 256 bytes
+  // of that row.  The fragment of lane l for k-step 4c + t (row r = l mod 16, chunk
+  // k = 4t + l/16, i.e. elements 32(4c+t) + 8(l/16), the same k mapping as the VGPR path)
+  // is at 1024 (r/4) + 16 (16 (r mod 4) + (k xor r)): the xor spreads the 16 rows that
+  // read together over all the banks.
+  uint32_t vq[4], rdo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 4 * q + (lane >> 4);
+    vq[q] = uint32_t(row) * wrowbytes + uint32_t(w * NKS * 64) + uint32_t((lane & 15) ^ row) * 16u;
+    const int r = lane & 15, k = 4 * q + (lane >> 4);
+    rdo[q] = uint32_t((r >> 2) * 1024 + ((r & 3) * 16 + (k ^ r)) * 16);
+  }
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const char* const ring_w = reinterpret_cast<const char*>(wring) + wu * (RQ * 4096);
+  const uint32_t ring_lds = lds_addr(ring_w);
+  const Srd wsrd = make_srd(static_cast<const char*>(a.W) + (size_t)r0 * wrowbytes,
+                            (uint64_t)(r1 - r0) * wrowbytes);
+  auto issue_quarter = [&](int slot, int n) {  // quarter n of this workgroup's stream
+    const int g = n / NQ, c = n - g * NQ;
+    const uint32_t base = uint32_t(g) * 16u * wrowbytes + uint32_t(c) * 256u;
+    const uint32_t sb = ring_lds + uint32_t(slot) * 4096u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16_nt(wsrd, sb + q * 1024u, vq[q] + base);
   };
 
   // ---- RMSNorm of the rows of this pass ----------------------------------------------
@@ -521,9 +610,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   // Every wave's hidden-state requests go out before any wave's W requests: the compute
   // unit's memory pipeline serves them in order, and the norm waits on the slowest wave.
   __syncthreads();
-  uint4 fr[D];
+  uint4 fr[LDSW ? 1 : D];
+  if constexpr (LDSW) {
 #pragma unroll
-  for (int j = 0; j < D; ++j) fr[j] = wload(0, j);
+    for (int j = 0; j < RQ; ++j) issue_quarter(j, j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < D; ++j) fr[j] = wload(0, j);
+  }
+  int slot = 0;  // ring slot of the next quarter
 
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
@@ -607,6 +702,27 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     }
     stat_init(st[e]);
   }
+  // Staged path: wave 0 moves a group's draft logits (softmax proposal) into LDS one
+  // group ahead, NGI DMA loads in which lane p takes token 4i + p/16, column p mod 16.
+  const bool gdma = LDSW && a.want_q;
+  const bool w0 = wu == 0;
+  const Srd qsrd = make_srd(a.G + (size_t)qrow0 * V, (uint64_t)qrows * (uint64_t)V * 4u);
+  uint32_t gqo[LDSW ? NGI : 1];
+#pragma unroll
+  for (int i = 0; i < (LDSW ? NGI : 1); ++i) {
+    const int jt = 4 * i + (lane >> 4);
+    gqo[i] = kOutOfRange;
+    if (a.want_q && jt < NTOK && jt < rows) {
+      const int row = row0 + jt, b = row / (a.K + 1), ir = row - b * (a.K + 1);
+      if (ir < a.K) gqo[i] = uint32_t(b * a.K + ir - qrow0) * uint32_t(V) * 4u + uint32_t(lane & 15) * 4u;
+    }
+  }
+  auto issue_gv = [&](int g) {
+    const uint32_t cb = uint32_t(r0 + int64_t(g) * 16) * 4u;
+    const uint32_t dst = lds_addr(&gvs[g & 1][0][0]);
+#pragma unroll
+    for (int i = 0; i < (LDSW ? NGI : 1); ++i) dma4(qsrd, dst + uint32_t(i) * 256u, gqo[i] + cb);
+  };
 
   int buf = 0;
   int gb = 0;  // first group of the staged run
@@ -615,8 +731,10 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     const int64_t v = r0 + g * 16 + ii;
     const bool vok = v < r1;
     float gv[NEP];
+    if constexpr (!LDSW) {
 #pragma unroll
-    for (int e = 0; e < NEP; ++e) gv[e] = bload4f(qr, qoff[e] + uint32_t(v) * 4u);
+      for (int e = 0; e < NEP; ++e) gv[e] = bload4f(qr, qoff[e] + uint32_t(v) * 4u);
+    }
     const float wsc = DT == JSV_FP8 ? bload4f(sr, uint32_t(g * 16 + ii) * 4u) : 1.f;
     floatx4 acc[NT1];
     float xacc[NX1];
@@ -624,26 +742,55 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     for (int t = 0; t < NT1; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int x = 0; x < NX1; ++x) xacc[x] = 0.f;
+    if constexpr (LDSW) {
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const uint4 fw = fr[u % D];
+      for (int c = 0; c < NQ; ++c) {
+        // This quarter's 4 DMA loads have landed: 4 (RQ - 1) loads of later quarters were
+        // issued after them, and on wave 0 in the first RQ quarters also the NGI
+        // draft-logit loads of this group.
+        if (gdma && w0 && c < RQ) wait_vmcnt<4 * (RQ - 1) + NGI>();
+        else wait_vmcnt<4 * (RQ - 1)>();
+        const char* sb = ring_w + slot * 4096;
 #pragma unroll
-      for (int h = 0; h < SPL; ++h) {
-        const int s = u * SPL + h;
-        if constexpr (FIRST) {
-          const uint4 gq = gsh[kofs(s) / EPL];
+        for (int t = 0; t < 4; ++t) {
+          const int s = 4 * c + t;
+          if constexpr (FIRST) {
+            const uint4 gq = gsh[kofs(s) / EPL];
 #pragma unroll
-          for (int t = 0; t < NT; ++t) xf[t][s] = norm_pack<XD>(xf[t][s], gq, rt[t]);
+            for (int tt = 0; tt < NT; ++tt) xf[tt][s] = norm_pack<XD>(xf[tt][s], gq, rt[tt]);
+          }
+          const uint4 f = *reinterpret_cast<const uint4*>(sb + rdo[t]);
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_step<XD>(f, xf[tt][s], acc[tt]);
+#pragma unroll
+          for (int x = 0; x < NX; ++x) xacc[x] = dot16<XD>(f, xrow[x][kofs(s) / EPL], xacc[x]);
         }
-        const uint4 f = wfrag<DT>(fw, h);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = mfma_step<XD>(f, xf[t][s], acc[t]);
-#pragma unroll
-        for (int x = 0; x < NX; ++x) xacc[x] = dot16<XD>(f, xrow[x][kofs(s) / EPL], xacc[x]);
+        wait_lgkmcnt0();  // the slot has been read: refill it RQ quarters ahead
+        issue_quarter(slot, g * NQ + c + RQ);
+        slot = slot + 1 == RQ ? 0 : slot + 1;
       }
-      // refill this slot D loads ahead (past the last group the loads read zeros)
-      const bool nxt = (u + D) >= NL;
-      fr[u % D] = wload(nxt ? g + 1 : g, nxt ? (u + D - NL) : (u + D));
+    } else {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const uint4 fw = fr[u % D];
+#pragma unroll
+        for (int h = 0; h < SPL; ++h) {
+          const int s = u * SPL + h;
+          if constexpr (FIRST) {
+            const uint4 gq = gsh[kofs(s) / EPL];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) xf[t][s] = norm_pack<XD>(xf[t][s], gq, rt[t]);
+          }
+          const uint4 f = wfrag<DT>(fw, h);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = mfma_step<XD>(f, xf[t][s], acc[t]);
+#pragma unroll
+          for (int x = 0; x < NX; ++x) xacc[x] = dot16<XD>(f, xrow[x][kofs(s) / EPL], xacc[x]);
+        }
+        // refill this slot D loads ahead (past the last group the loads read zeros)
+        const bool nxt = (u + D) >= NL;
+        fr[u % D] = wload(nxt ? g + 1 : g, nxt ? (u + D - NL) : (u + D));
+      }
     }
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
@@ -652,7 +799,15 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) red[buf][w][t][lane] = acc[t];
+    if constexpr (LDSW) {
+      if (gdma && w0) wait_vmcnt<NKS>();  // this group's draft logits: NKS loads since
+    }
     __syncthreads();
+    if constexpr (LDSW) {
+      if (gdma && w0) issue_gv(g + 1);
+#pragma unroll
+      for (int e = 0; e < NEP; ++e) gv[e] = qrow[e] ? gvs[g & 1][jj[e]][ii] : 0.f;
+    }
 #pragma unroll
     for (int e = 0; e < NEP; ++e) {
       if (jj[e] >= NTOK) continue;
@@ -701,8 +856,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     }
     buf ^= 1;
   };
+  if constexpr (LDSW) {
+    if (gdma && w0) issue_gv(0);
+  }
   group(0, Tag<true>{});
   for (int g = 1; g < ng; ++g) group(g, Tag<false>{});
+  if constexpr (LDSW) wait_vmcnt<0>();  // no DMA write into LDS may outlive the workgroup
 
   if (!a.stats) return;
 #pragma unroll

@@ -42,6 +42,8 @@ def qwen(dev):
     (1024, 256, synth.F32, 5), (1000, 256, synth.BF16, 3), (4099, 512, synth.BF16, 17),
     (2048, 4096, synth.BF16, 40), (777, 5120, synth.BF16, 33), (300, 1024, synth.F32, 1),
     (4099, 512, synth.FP8, 17), (1000, 5120, synth.FP8, 33),
+    # bf16 heads staged through LDS with fewer quarters per group than ring slots
+    (3001, 1024, synth.BF16, 17), (2050, 2048, synth.BF16, 1), (5003, 3072, synth.BF16, 16),
 ])
 def test_lmhead_logits(dev, V, d, dtype, rows):
     say(f"lmhead V={V} d={d} {dtype} rows={rows}")
@@ -171,6 +173,24 @@ def test_verify_qwen8b_k32_b4(qwen, dev):
         say(f"qwen8b K=32 B=4 verify T={T}")
         blk = synth.make_block(qwen.cpu, cfg.batch, cfg.K, cfg.sigma, T, seed=40 + int(T))
         got, ref = run_verify(qwen, blk, T, SOFT, 5, 9, ws)
+        compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+        compare_logits(got["logits"], ref["logits"], st)
+    say(f"  {st}")
+    assert st["exact"] >= 6
+
+
+def test_verify_ragged_vocab_staged_head(dev):
+    """bf16 head with d = 1024 (one quarter per group, three ring slots), a ragged
+    vocabulary and two passes of 17 rows; softmax proposal at T = 1, so the draft logits
+    travel by DMA too."""
+    head = synth.random_head(3001, 1024, synth.BF16, seed=31)
+    case = Case(head, dev)
+    ws = jsv.new_workspace(case.gpu, 2, 16)
+    st = new_stats()
+    for seed in range(4):
+        say(f"ragged V=3001 d=1024 B=2 K=16 seed={seed}")
+        blk = synth.make_block(head, 2, 16, 0.5, 1.0, seed=seed)
+        got, ref = run_verify(case, blk, 1.0, SOFT, seed, 1, ws)
         compare_verify(got, ref, blk.draft_tokens.numpy(), st)
         compare_logits(got["logits"], ref["logits"], st)
     say(f"  {st}")
