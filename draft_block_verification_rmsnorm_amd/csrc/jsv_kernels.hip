@@ -475,11 +475,13 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   constexpr int NL = NKS / SPL;                         // W loads per group and lane
   constexpr int D = DT == JSV_FP8 ? NL : pick_window(NT, NKS);  // W loads in flight
   static_assert(NL * SPL == NKS && NL >= 1, "fp8 needs an even number of k-steps");
-  // bf16 with whole quarters (4 k-steps, 128 elements) in a wave's slice: W goes to LDS
-  // by DMA loads that each read 4 rows x 256 contiguous bytes, whole cache lines and
-  // non-temporal, RQ quarters ahead; the MFMA fragments are read back from LDS.
-  constexpr bool LDSW = DT == JSV_BF16 && NKS % 4 == 0;
-  constexpr int NQ = NKS / 4 > 0 ? NKS / 4 : 1;  // quarters per slice
+  // bf16 and fp8 heads with whole quarters (4 loads of 16 bytes per lane: 4 k-steps of
+  // bf16, 8 of fp8; 256 bytes of each row) in a wave's slice: W goes to LDS by DMA loads
+  // that each read 4 rows x 256 contiguous bytes, whole cache lines and non-temporal, RQ
+  // quarters ahead; the MFMA fragments are read back from LDS.
+  constexpr bool LDSW = (DT == JSV_BF16 || DT == JSV_FP8) && NL % 4 == 0;
+  constexpr int NQ = NL / 4 > 0 ? NL / 4 : 1;   // quarters per slice
+  constexpr int NSC = DT == JSV_FP8 ? 1 : 0;    // row-scale DMA loads per group
   constexpr int RQ = NT <= 1 ? 3 : 2;           // 4 KB quarter slots per wave
   constexpr int NTOK = NT * 16 + NX;
   constexpr int NGI = (NTOK + 3) / 4;       // 256-byte DMA loads of a group's draft logits
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   constexpr int SF = stage_groups(NTOK, 2 * kWaves * NT1 * kWave * 16 + 2 * kWaves * NX1 * 16 * 4 +
                                             NX1 * XLEN * 16 + XLEN * 16 + kWaves * kRowsPerPass * 8 +
                                             kRowsPerPass * 4 + 16 + RING * 16 +
-                                            (LDSW ? 2 * NGI * 4 * 16 * 4 : 64));
+                                            (LDSW ? 2 * NGI * 4 * 16 * 4 : 64) + 512);
   static_assert(SF >= 1, "LDS");
   static_assert(NTOK >= 1 && NTOK <= kRowsPerPass && NX <= 1, "tiling");
   __shared__ floatx4 red[2][kWaves][NT1][kWave];
@@ -503,6 +505,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
   __shared__ float rnorm[kRowsPerPass];
   __shared__ uint4 wring[RING];
   __shared__ float gvs[LDSW ? 2 : 1][LDSW ? NGI * 4 : 1][16];
+  __shared__ float wss[LDSW && NSC ? 2 : 1][64];  // fp8 row scales of a group (16 used)
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   // Workgroup -> (vocabulary chunk, pass of rows).  The passes of one chunk sit on the
@@ -557,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = 4 * q + (lane >> 4);
-    vq[q] = uint32_t(row) * wrowbytes + uint32_t(w * NKS * 64) + uint32_t((lane & 15) ^ row) * 16u;
+    vq[q] = uint32_t(row) * wrowbytes + uint32_t(w * NL * 64) + uint32_t((lane & 15) ^ row) * 16u;
     const int r = lane & 15, k = 4 * q + (lane >> 4);
     rdo[q] = uint32_t((r >> 2) * 1024 + ((r & 3) * 16 + (k ^ r)) * 16);
   }
@@ -717,12 +720,21 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
       if (ir < a.K) gqo[i] = uint32_t(b * a.K + ir - qrow0) * uint32_t(V) * 4u + uint32_t(lane & 15) * 4u;
     }
   }
-  auto issue_gv = [&](int g) {
-    const uint32_t cb = uint32_t(r0 + int64_t(g) * 16) * 4u;
-    const uint32_t dst = lds_addr(&gvs[g & 1][0][0]);
+  const Srd ssrd = make_srd(DT == JSV_FP8 ? a.wscale + r0 : a.logits,
+                            DT == JSV_FP8 ? uint64_t(r1 - r0) * 4u : 0u);
+  // Wave 0's per-group side loads, one group ahead: the draft logits (softmax proposal,
+  // NGI loads) and an fp8 head's 16 row scales (one load, lanes 0-15).
+  auto issue_side = [&](int g) {
+    if (gdma) {
+      const uint32_t cb = uint32_t(r0 + int64_t(g) * 16) * 4u;
+      const uint32_t dst = lds_addr(&gvs[g & 1][0][0]);
 #pragma unroll
-    for (int i = 0; i < (LDSW ? NGI : 1); ++i) dma4(qsrd, dst + uint32_t(i) * 256u, gqo[i] + cb);
+      for (int i = 0; i < (LDSW ? NGI : 1); ++i) dma4(qsrd, dst + uint32_t(i) * 256u, gqo[i] + cb);
+    }
+    if constexpr (NSC > 0)
+      dma4(ssrd, lds_addr(&wss[g & 1][0]), lane < 16 ? uint32_t(g * 16 + lane) * 4u : kOutOfRange);
   };
+  const bool side = gdma || NSC > 0;  // wave 0 issues side loads
 
   int buf = 0;
   int gb = 0;  // first group of the staged run
@@ -735,7 +747,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
       for (int e = 0; e < NEP; ++e) gv[e] = bload4f(qr, qoff[e] + uint32_t(v) * 4u);
     }
-    const float wsc = DT == JSV_FP8 ? bload4f(sr, uint32_t(g * 16 + ii) * 4u) : 1.f;
+    float wsc = 1.f;
+    if constexpr (DT == JSV_FP8 && !LDSW) wsc = bload4f(sr, uint32_t(g * 16 + ii) * 4u);
     floatx4 acc[NT1];
     float xacc[NX1];
 #pragma unroll
@@ -746,24 +759,32 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
       for (int c = 0; c < NQ; ++c) {
         // This quarter's 4 DMA loads have landed: 4 (RQ - 1) loads of later quarters were
-        // issued after them, and on wave 0 in the first RQ quarters also the NGI
-        // draft-logit loads of this group.
-        if (gdma && w0 && c < RQ) wait_vmcnt<4 * (RQ - 1) + NGI>();
-        else wait_vmcnt<4 * (RQ - 1)>();
+        // issued after them, and on wave 0 in the first RQ quarters also this group's side
+        // loads.
+        if (side && w0 && c < RQ) {
+          if (gdma) wait_vmcnt<4 * (RQ - 1) + NGI + NSC>();
+          else wait_vmcnt<4 * (RQ - 1) + NSC>();
+        } else {
+          wait_vmcnt<4 * (RQ - 1)>();
+        }
         const char* sb = ring_w + slot * 4096;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int s = 4 * c + t;
-          if constexpr (FIRST) {
-            const uint4 gq = gsh[kofs(s) / EPL];
+          const uint4 fw = *reinterpret_cast<const uint4*>(sb + rdo[t]);
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) xf[tt][s] = norm_pack<XD>(xf[tt][s], gq, rt[tt]);
+          for (int h = 0; h < SPL; ++h) {
+            const int s = (4 * c + t) * SPL + h;
+            if constexpr (FIRST) {
+              const uint4 gq = gsh[kofs(s) / EPL];
+#pragma unroll
+              for (int tt = 0; tt < NT; ++tt) xf[tt][s] = norm_pack<XD>(xf[tt][s], gq, rt[tt]);
+            }
+            const uint4 f = wfrag<DT>(fw, h);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_step<XD>(f, xf[tt][s], acc[tt]);
+#pragma unroll
+            for (int x = 0; x < NX; ++x) xacc[x] = dot16<XD>(f, xrow[x][kofs(s) / EPL], xacc[x]);
           }
-          const uint4 f = *reinterpret_cast<const uint4*>(sb + rdo[t]);
-#pragma unroll
-          for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_step<XD>(f, xf[tt][s], acc[tt]);
-#pragma unroll
-          for (int x = 0; x < NX; ++x) xacc[x] = dot16<XD>(f, xrow[x][kofs(s) / EPL], xacc[x]);
         }
         wait_lgkmcnt0();  // the slot has been read: refill it RQ quarters ahead
         issue_quarter(slot, g * NQ + c + RQ);
@@ -800,13 +821,14 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) red[buf][w][t][lane] = acc[t];
     if constexpr (LDSW) {
-      if (gdma && w0) wait_vmcnt<NKS>();  // this group's draft logits: NKS loads since
+      if (side && w0) wait_vmcnt<NL>();  // this group's side loads: NL W loads since
     }
     __syncthreads();
     if constexpr (LDSW) {
-      if (gdma && w0) issue_gv(g + 1);
+      if (side && w0) issue_side(g + 1);
 #pragma unroll
       for (int e = 0; e < NEP; ++e) gv[e] = qrow[e] ? gvs[g & 1][jj[e]][ii] : 0.f;
+      if constexpr (NSC > 0) wsc = wss[g & 1][ii];
     }
 #pragma unroll
     for (int e = 0; e < NEP; ++e) {
@@ -857,7 +879,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     buf ^= 1;
   };
   if constexpr (LDSW) {
-    if (gdma && w0) issue_gv(0);
+    if (side && w0) issue_side(0);
   }
   group(0, Tag<true>{});
   for (int g = 1; g < ng; ++g) group(g, Tag<false>{});

@@ -44,6 +44,7 @@ def qwen(dev):
     (4099, 512, synth.FP8, 17), (1000, 5120, synth.FP8, 33),
     # bf16 heads staged through LDS with fewer quarters per group than ring slots
     (3001, 1024, synth.BF16, 17), (2050, 2048, synth.BF16, 1), (5003, 3072, synth.BF16, 16),
+    (3001, 2048, synth.FP8, 17), (1500, 4096, synth.FP8, 33), (777, 4096, synth.FP8, 1),
 ])
 def test_lmhead_logits(dev, V, d, dtype, rows):
     say(f"lmhead V={V} d={d} {dtype} rows={rows}")
