@@ -1299,13 +1299,13 @@ __global__ __launch_bounds__(kSliceThreads) void slice_sum_kernel(SampleArgs a) 
 
 // Bonus sampler, part 2: grid B, one wave.  t = v_k * Z is located among the slice
 // totals (rounds of 64 slices: a running base plus a wave prefix sum), then inside the
-// chosen slice (rounds of 64 consecutive columns): the token is the first column whose
+// chosen slice (16 consecutive columns per lane): the token is the first column whose
 // CDF exceeds t.  Both passes over the slice totals form every sum in the same order,
 // so the CDF they walk ends exactly at the Z that t was taken from.
 constexpr int kLocRounds = 4;  // slice-total rounds kept in registers (V <= 262144)
 
 __global__ __launch_bounds__(kWave) void locate_kernel(SampleArgs a) {
-  constexpr int CR = kSampleSlice / kWave;  // column rounds inside a slice
+  constexpr int CR = kSampleSlice / kWave;  // columns per lane inside a slice
   const int b = blockIdx.x, lane = threadIdx.x;
   const int NB = sample_slices(a.f.V), rounds = (NB + kWave - 1) / kWave;
   const rsrc_t zsr = make_rsrc(a.zs + (size_t)b * NB * 2, uint64_t(NB) * 16u);
@@ -1365,39 +1365,56 @@ __global__ __launch_bounds__(kWave) void locate_kernel(SampleArgs a) {
   bool fall = s < 0;  // rounding left t at or above the last step: take the last mass
   if (fall) { s = slast; sbase = slast_base; }
 
-  // inside slice s: round e covers columns c0 + 64 e + lane
+  // Inside slice s, lane l takes the CR consecutive columns c0 + CR l + j: each lane sums
+  // its own columns in order, one wave scan places the lanes, and every lane walks its
+  // columns against t in parallel; the token is the first (lane, column) whose CDF
+  // exceeds t.
   const uint32_t rowbytes = uint32_t(V) * 4u;
   const rsrc_t zr = make_rsrc(a.logits + (size_t)row * V, rowbytes);
   const rsrc_t gr = make_rsrc(rm.use_q ? a.G + (size_t)(b * K + k) * V : a.logits,
                               rm.use_q ? rowbytes : 0u);
-  const int64_t c0 = (int64_t)s * kSampleSlice;
+  const int64_t c0 = (int64_t)s * kSampleSlice, cl = c0 + int64_t(lane) * CR;
   float z[CR], g[CR];
 #pragma unroll
   for (int e = 0; e < CR; ++e) {
-    const uint32_t off = uint32_t(c0 + e * kWave + lane) * 4u;
+    const uint32_t off = uint32_t(cl + e) * 4u;
     z[e] = bload4f(zr, off);
     g[e] = bload4f(gr, off);
   }
-  int tok = -1, lastpos = -1;
-  double C = sbase, clo = 0.0, chi = 0.0;
+  double x[CR];
+  double own = 0.0;  // this lane's columns, summed in column order
 #pragma unroll
   for (int e = 0; e < CR; ++e) {
-    const int64_t v = c0 + e * kWave + lane;
+    const int64_t v = cl + e;
     double r = 0.0, p = 0.0;
-    if (v >= 0 && v < V) rm.eval(v, z[e], g[e], r, p);
-    const double x = zero ? p : r;
-    const double inc = wave_incl_scan(x);
-    const double hi = C + inc;
-    const uint64_t hit = (tok < 0 && !fall) ? __ballot(x > 0.0 && hi > t) : 0ull;
-    const uint64_t pos = __ballot(x > 0.0);
-    if (hit) {
-      const int l = __builtin_ctzll(hit);
-      tok = int(c0 + e * kWave + l);
-      chi = readlane_d(hi, l);
-      clo = chi - readlane_d(x, l);
+    if (s >= 0 && v < V) rm.eval(v, z[e], g[e], r, p);
+    x[e] = zero ? p : r;
+    own += x[e];
+  }
+  const double lbase = sbase + (wave_incl_scan(own) - own);  // CDF before this lane's columns
+  int je = -1, jl = -1;  // first column whose CDF exceeds t; last column with mass
+  double C = lbase, clo = 0.0, chi = 0.0;
+#pragma unroll
+  for (int e = 0; e < CR; ++e) {
+    const double lo = C;
+    C += x[e];
+    if (x[e] > 0.0) {
+      jl = e;
+      if (je < 0 && C > t) { je = e; clo = lo; chi = C; }
     }
-    if (pos) lastpos = int(c0 + e * kWave + 63 - __builtin_clzll(pos));
-    C += readlane_d(inc, kWave - 1);
+  }
+  int tok = -1, lastpos = -1;
+  const uint64_t hit = fall ? 0ull : __ballot(je >= 0);
+  if (hit) {
+    const int l = __builtin_ctzll(hit);
+    tok = int(c0) + l * CR + readlane_i(je, l);
+    clo = readlane_d(clo, l);
+    chi = readlane_d(chi, l);
+  }
+  const uint64_t pos = __ballot(jl >= 0);
+  if (pos) {
+    const int l = 63 - __builtin_clzll(pos);
+    lastpos = int(c0) + l * CR + readlane_i(jl, l);
   }
   uint32_t f = zero ? uint32_t(JSV_FLAG_ZERO_RESIDUAL) : 0u;
   if (tok >= 0) {
