@@ -60,9 +60,34 @@ jsv_status check_block(int32_t B, int32_t K, float T, int32_t mode) {
 // Workgroups of the LM-head kernel: one per CU, at most one per 16-row vocabulary group.
 jsv_status run_stats(const jsv_lm_head* head, int nks, const void* hidden, int M, float* logits,
                      const float* G, int B, int K, float T, int mode, int stats, RowStat* partial,
-                     float* rnorm, hipStream_t stream) {
+                     float* rnorm, char* ws, hipStream_t stream) {
   const int cus = device_cu_count();
   if (cus <= 0) return JSV_EHIP;
+  if (stats && ws != nullptr && wide_eligible(head->dtype, head->hidden, M)) {
+    // More rows than one pass holds: split d instead of the rows (W is read once).
+    const WsLayout L = ws_layout(head->vocab, B, K, 0, head->hidden, head->dtype);
+    WideArgs w{};
+    w.W = head->weight;
+    w.gamma = head->norm_weight;
+    w.hidden = hidden;
+    w.V = head->vocab;
+    w.d = int(head->hidden);
+    w.M = M;
+    w.eps = head->eps;
+    w.pl = plan_wide(head->vocab, head->hidden, M, cus);
+    w.xhat = reinterpret_cast<uint16_t*>(ws + L.xhat);
+    w.planes = reinterpret_cast<float*>(ws + L.planes);
+    w.rnorm = rnorm;
+    w.logits = logits;
+    w.G = G;
+    w.B = B;
+    w.K = K;
+    w.T = T;
+    w.c = T > 0.f ? kLog2e / T : 0.f;
+    w.want_q = (mode == JSV_PROPOSAL_SOFTMAX && T > 0.f && G != nullptr) ? 1 : 0;
+    w.partial = partial;
+    return launch_wide(w, stream) == hipSuccess ? JSV_OK : JSV_EHIP;
+  }
   StatsArgs a{};
   a.W = head->weight;
   a.wscale = head->dtype == JSV_FP8 ? head->weight_scale : nullptr;
@@ -115,7 +140,10 @@ FinalArgs final_args(const jsv_lm_head* head, const void* hidden, const int32_t*
   f.mode = mode;
   f.kind = kind;
   const int cus = device_cu_count();
-  f.P = cus > 0 ? plan_stats(head->vocab, B * (K + 1), cus).nchunk : 0;
+  const int M = B * (K + 1);
+  f.P = cus <= 0 ? 0
+        : wide_eligible(head->dtype, head->hidden, M) ? plan_wide(head->vocab, head->hidden, M, cus).ncomb
+                                                      : plan_stats(head->vocab, M, cus).nchunk;
   f.partial = reinterpret_cast<const RowStat*>(ws + L.partial);
   f.rowstat = reinterpret_cast<RowStat*>(ws + L.rowstat);
   f.dlog = reinterpret_cast<DraftLogit*>(ws + L.dlog);
@@ -125,8 +153,8 @@ FinalArgs final_args(const jsv_lm_head* head, const void* hidden, const int32_t*
   return f;
 }
 
-size_t needed_bytes(int64_t V, int B, int K, int top_n, bool logits_in_ws) {
-  const WsLayout L = ws_layout(V, B, K, top_n);
+size_t needed_bytes(const jsv_lm_head* head, int B, int K, int top_n, bool logits_in_ws) {
+  const WsLayout L = ws_layout(head->vocab, B, K, top_n, head->hidden, head->dtype);
   return logits_in_ws ? L.total : L.logits;
 }
 
@@ -151,7 +179,7 @@ size_t jsv_workspace_bytes(const jsv_lm_head* head, int32_t batch, int32_t K, in
   int nks = 0;
   if (check_head(head, &nks) != JSV_OK) return 0;
   if (batch < 1 || batch > kMaxB || K < 1 || K > kMaxK || top_n < 0 || top_n > kMaxTopN) return 0;
-  return needed_bytes(head->vocab, batch, K, top_n, true);
+  return needed_bytes(head, batch, K, top_n, true);
 }
 
 jsv_status jsv_lmhead_logits(const jsv_lm_head* head, const void* hidden, int64_t rows,
@@ -167,7 +195,7 @@ jsv_status jsv_lmhead_logits(const jsv_lm_head* head, const void* hidden, int64_
   if (rows > INT32_MAX / 2) return JSV_EUNSUPPORTED;
   (void)hipGetLastError();
   return run_stats(head, nks, hidden, int(rows), logits, nullptr, 0, -1, 0.f, JSV_PROPOSAL_POINT,
-                   0, nullptr, nullptr, static_cast<hipStream_t>(hip_stream));
+                   0, nullptr, nullptr, nullptr, static_cast<hipStream_t>(hip_stream));
 }
 
 static jsv_status verify_prepare(const jsv_lm_head* head, const void* hidden,
@@ -184,7 +212,7 @@ static jsv_status verify_prepare(const jsv_lm_head* head, const void* hidden,
   if (n_accepted == nullptr) return JSV_EINVAL;
   if (mode == JSV_PROPOSAL_SOFTMAX && T > 0.f && draft_logits == nullptr) return JSV_EINVAL;
   if (!aligned16(ws)) return JSV_EINVAL;
-  if (ws_bytes < needed_bytes(head->vocab, B, K, 0, logits_out == nullptr)) return JSV_EWORKSPACE;
+  if (ws_bytes < needed_bytes(head, B, K, 0, logits_out == nullptr)) return JSV_EWORKSPACE;
   return JSV_OK;
 }
 
@@ -202,12 +230,12 @@ jsv_status jsv_verify_stats(const jsv_lm_head* head, const void* hidden,
                                  n_accepted, committed, logits_out, ws, ws_bytes, &nks);
   if (st != JSV_OK) return st;
   (void)hipGetLastError();
-  const WsLayout L = ws_layout(head->vocab, B, K, 0);
+  const WsLayout L = ws_layout(head->vocab, B, K, 0, head->hidden, head->dtype);
   char* w = static_cast<char*>(ws);
   float* logits = logits_out ? logits_out : reinterpret_cast<float*>(w + L.logits);
   return run_stats(head, nks, hidden, B * (K + 1), logits, draft_logits, B, K, temperature, mode, 1,
                    reinterpret_cast<RowStat*>(w + L.partial), reinterpret_cast<float*>(w + L.rnorm),
-                   static_cast<hipStream_t>(hip_stream));
+                   w, static_cast<hipStream_t>(hip_stream));
 }
 
 jsv_status jsv_verify_sample(const jsv_lm_head* head, const void* hidden,
@@ -222,7 +250,7 @@ jsv_status jsv_verify_sample(const jsv_lm_head* head, const void* hidden,
   if (st != JSV_OK) return st;
   (void)hipGetLastError();
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  const WsLayout L = ws_layout(head->vocab, B, K, 0);
+  const WsLayout L = ws_layout(head->vocab, B, K, 0, head->hidden, head->dtype);
   char* w = static_cast<char*>(ws);
   FinalArgs f = final_args(head, hidden, draft_tokens, draft_logits, B, K, temperature, mode,
                            kFinalizeVerify, w, L);
@@ -275,15 +303,15 @@ jsv_status jsv_score_outcomes(const jsv_lm_head* head, const void* hidden_pred,
   if (out_len == nullptr || out_token == nullptr || out_prob == nullptr) return JSV_EINVAL;
   if (ws == nullptr || !aligned16(ws)) return JSV_EINVAL;
   if (mode == JSV_PROPOSAL_SOFTMAX && temperature > 0.f && draft_logits == nullptr) return JSV_EINVAL;
-  if (ws_bytes < needed_bytes(head->vocab, B, K, top_n, true)) return JSV_EWORKSPACE;
+  if (ws_bytes < needed_bytes(head, B, K, top_n, true)) return JSV_EWORKSPACE;
   (void)hipGetLastError();
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  const WsLayout L = ws_layout(head->vocab, B, K, top_n);
+  const WsLayout L = ws_layout(head->vocab, B, K, top_n, head->hidden, head->dtype);
   char* w = static_cast<char*>(ws);
   float* logits = reinterpret_cast<float*>(w + L.logits);
   st = run_stats(head, nks, hidden_pred, B * (K + 1), logits, draft_logits, B, K, temperature, mode,
                  1, reinterpret_cast<RowStat*>(w + L.partial), reinterpret_cast<float*>(w + L.rnorm),
-                 stream);
+                 w, stream);
   if (st != JSV_OK) return st;
   FinalArgs f = final_args(head, hidden_pred, draft_tokens, draft_logits, B, K, temperature, mode,
                            kFinalizeScore, w, L);
@@ -330,14 +358,14 @@ jsv_status jsv_anchor_replace(const jsv_lm_head* head, const void* hidden_pred,
   if (hidden_pred == nullptr || !aligned16(hidden_pred) || draft_tokens == nullptr ||
       position == nullptr || token == nullptr || ws == nullptr || !aligned16(ws))
     return JSV_EINVAL;
-  if (ws_bytes < needed_bytes(head->vocab, B, K, 0, true)) return JSV_EWORKSPACE;
+  if (ws_bytes < needed_bytes(head, B, K, 0, true)) return JSV_EWORKSPACE;
   (void)hipGetLastError();
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  const WsLayout L = ws_layout(head->vocab, B, K, 0);
+  const WsLayout L = ws_layout(head->vocab, B, K, 0, head->hidden, head->dtype);
   char* w = static_cast<char*>(ws);
   st = run_stats(head, nks, hidden_pred, B * (K + 1), reinterpret_cast<float*>(w + L.logits),
                  nullptr, B, K, 0.f, JSV_PROPOSAL_POINT, 1, reinterpret_cast<RowStat*>(w + L.partial),
-                 reinterpret_cast<float*>(w + L.rnorm), stream);
+                 reinterpret_cast<float*>(w + L.rnorm), w, stream);
   if (st != JSV_OK) return st;
   FinalArgs f = final_args(head, hidden_pred, draft_tokens, nullptr, B, K, 0.f, JSV_PROPOSAL_POINT,
                            kFinalizeAnchor, w, L);

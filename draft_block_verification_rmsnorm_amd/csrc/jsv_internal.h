@@ -84,13 +84,50 @@ __host__ __device__ inline int score_slices(int64_t V) {
 }
 
 struct WsLayout {
-  size_t req, rowfinal, rowstat, dlog, rnorm, partial, zs, cand, logits, total;
+  size_t req, rowfinal, rowstat, dlog, rnorm, partial, zs, cand, xhat, planes, logits, total;
 };
+
+// LM head for more rows than one pass holds (bf16 W, 34..144 rows, d a multiple of 1024,
+// at most 5120): the reduction dimension is split into blocks of 1024 columns instead of
+// the rows into passes, so W is read once.  Workgroup (vocabulary chunk, block) holds
+// every row's normalised states over its block, one 16-row tile per wave, and writes fp32
+// partial products; a second kernel sums the blocks, writes the logits and forms the
+// per-row partial statistics.
+constexpr int kWideBlock = 1024;     // columns of d per block
+constexpr int kWideMaxRows = 144;    // nine 16-row tiles
+constexpr int kWideMaxD = 5120;      // at most five blocks
+inline bool wide_eligible(int dtype, int64_t d, int M) {
+  return dtype == 0 /* JSV_BF16 */ && M > kRowsPerPass && M <= kWideMaxRows &&
+         d % kWideBlock == 0 && d <= kWideMaxD;
+}
+struct WidePlan {
+  int nw;      // waves (tiles) of the product kernel: 8 or 9
+  int mp;      // rows of a partial plane: M rounded up to whole tiles
+  int S;       // blocks of d
+  int nchunk;  // vocabulary chunks of the product kernel
+  int ncomb;   // workgroups of the combine kernel (= partial statistics per row)
+};
+inline WidePlan plan_wide(int64_t V, int64_t d, int M, int cus) {
+  WidePlan p{};
+  p.nw = M <= 128 ? 8 : 9;  // eight waves move the eight quarters of a W group
+  p.mp = 16 * ((M + 15) / 16);
+  p.S = int(d / kWideBlock);
+  const int64_t ngroups = (V + 15) / 16;
+  int64_t nc = (cus > 0 ? cus : 1) / p.S;
+  if (nc < 1) nc = 1;
+  if (nc > ngroups) nc = ngroups;
+  p.nchunk = int(nc);
+  int64_t cb = cus < kMaxGrid ? cus : kMaxGrid;
+  const int64_t ntiles = (V + 63) / 64;
+  if (cb > ntiles) cb = ntiles;
+  p.ncomb = int(cb > 0 ? cb : 1);
+  return p;
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace carve-up for B requests of K drafts over vocabulary V, top_n outcomes.
-inline WsLayout ws_layout(int64_t V, int B, int K, int top_n) {
+inline WsLayout ws_layout(int64_t V, int B, int K, int top_n, int64_t d, int dtype) {
   const size_t M = size_t(B) * size_t(K + 1);
   WsLayout L{};
   size_t off = 0;
@@ -100,6 +137,11 @@ inline WsLayout ws_layout(int64_t V, int B, int K, int top_n) {
   L.dlog = off;     off = align256(off + M * sizeof(DraftLogit));
   L.rnorm = off;    off = align256(off + M * sizeof(float));
   L.partial = off;  off = align256(off + size_t(kMaxGrid) * M * sizeof(RowStat));
+  // Wide LM head only; before the sections whose size depends on top_n.
+  const bool wide = wide_eligible(dtype, d, int(M));
+  const WidePlan wp = plan_wide(V, d > 0 ? d : kWideBlock, int(M), 1);
+  L.xhat = off;     off = align256(off + (wide ? M * size_t(d) * 2 : 0));
+  L.planes = off;   off = align256(off + (wide ? size_t(wp.S) * size_t(V) * size_t(wp.mp) * 4 : 0));
   const size_t zs_sample = size_t(B) * size_t(sample_slices(V)) * 2 * sizeof(double);
   const size_t zs_score = M * size_t(score_slices(V)) * sizeof(double);
   L.zs = off;       off = align256(off + (zs_sample > zs_score ? zs_sample : zs_score));
@@ -220,6 +262,27 @@ struct ScoreArgs {
 // `nks` is hidden / (kWaves * elements per k-step); the launcher picks the instance.
 bool stats_supported(int dtype, int nks);
 hipError_t launch_stats(int dtype, int nks, int grid, const StatsArgs& a, hipStream_t stream);
+
+// The wide LM head (see wide_eligible): three launches on `stream`.
+struct WideArgs {
+  const void* W;          // [V][d] bf16
+  const void* gamma;      // [d]
+  const void* hidden;     // [M][d]
+  int64_t V;
+  int d, M;
+  float eps;
+  WidePlan pl;
+  uint16_t* xhat;         // [M][d] normalised rows (workspace)
+  float* planes;          // [S][V][mp] partial products (workspace)
+  float* rnorm;           // [M]
+  float* logits;          // [M][V]
+  const float* G;         // [B][K][V] draft logits, or null
+  int B, K;
+  float T, c;             // temperature and log2(e) / T
+  int want_q;
+  RowStat* partial;       // [M][ncomb]
+};
+hipError_t launch_wide(const WideArgs& a, hipStream_t stream);
 hipError_t launch_rowstat(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_scan(const FinalArgs& a, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t stream);

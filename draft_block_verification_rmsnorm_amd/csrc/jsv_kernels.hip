@@ -899,6 +899,232 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// Wide LM head (bf16, 34..144 rows).  Part 1: the normalised rows, one workgroup of 256
+// threads per row: r from the float64 sum of squares, x = bf16(fp32(fp32(h r) gamma)).
+__global__ __launch_bounds__(kSliceThreads) void xhat_kernel(WideArgs a) {
+  constexpr int PER = (kWideMaxD / 8 + kSliceThreads - 1) / kSliceThreads;  // 16-byte groups per thread
+  const int m = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const uint32_t rowbytes = uint32_t(a.d) * 2u;
+  const int n16 = a.d / 8;
+  const rsrc_t hr = make_rsrc(static_cast<const char*>(a.hidden) + (size_t)m * rowbytes, rowbytes);
+  const rsrc_t gr = make_rsrc(a.gamma, rowbytes);
+  uint4 hq[PER], gq[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int q = tid + j * kSliceThreads;
+    hq[j] = bload16(hr, q < n16 ? uint32_t(q) * 16u : kOutOfRange, 0);
+    gq[j] = bload16(gr, q < n16 ? uint32_t(q) * 16u : kOutOfRange, 0);
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) ss += sumsq16<JSV_BF16>(hq[j]);
+  ss = wave_sum(ss);
+  __shared__ double wsum[kSliceThreads / kWave];
+  if (lane == 0) wsum[w] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < kSliceThreads / kWave; ++i) tot += wsum[i];  // fixed order
+  const float r = rms_factor(tot, a.d, a.eps);
+  if (tid == 0) a.rnorm[m] = r;
+  uint4* xo = reinterpret_cast<uint4*>(a.xhat + (size_t)m * a.d);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int q = tid + j * kSliceThreads;
+    if (q < n16) xo[q] = norm_pack<JSV_BF16>(hq[j], gq[j], r);
+  }
+}
+
+// Part 2: partial products.  Workgroup (vocabulary chunk, block q of 1024 columns of d);
+// wave w holds tile w (rows 16w .. 16w + 15) of the normalised states over the block in
+// registers (32 MFMA k-steps) and every wave multiplies the same W group (16 vocabulary
+// rows x 1024 columns, 32 KB) from LDS.  The group is staged by DMA in eight quarters of
+// 4 k-steps, wave w < 8 moving quarter w in the layout of the LM-head kernel (4 rows x
+// 256 contiguous bytes per load, row-XOR swizzle), three groups ahead.  The products go to
+// plane q in [vocabulary][row] order straight from the accumulators: the waves of a group
+// fill whole rows of the plane between them.
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void wide_kernel(WideArgs a) {
+  constexpr int NQ = kWideBlock / 128;  // quarters of a group (4 k-steps of 32 columns)
+  constexpr int KS = kWideBlock / 32;   // k-steps of a block
+  constexpr int RG = 4;                 // groups in the LDS ring (RG - 1 ahead)
+  __shared__ uint4 ring[RG][NQ][256];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int S = a.pl.S, P = a.pl.nchunk, mp = a.pl.mp;
+  const int q = blockIdx.x % S, chunk = blockIdx.x / S;
+  const int64_t V = a.V;
+  const int64_t r0 = V * chunk / P, r1 = V * (chunk + 1) / P;
+  const int ng = int((r1 - r0 + 15) >> 4);
+  const uint32_t wrowbytes = uint32_t(a.d) * 2u;
+
+  // DMA of quarter wu of group g into ring slot g % RG (waves 0..7).
+  const Srd wsrd = make_srd(static_cast<const char*>(a.W) + (size_t)r0 * wrowbytes,
+                            (uint64_t)(r1 - r0) * wrowbytes);
+  uint32_t vq[4], rdo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    vq[i] = uint32_t(row) * wrowbytes + uint32_t(q) * (kWideBlock * 2u) + uint32_t(wu < NQ ? wu : 0) * 256u +
+            uint32_t((lane & 15) ^ row) * 16u;
+    const int r = lane & 15, k = 4 * i + (lane >> 4);
+    rdo[i] = uint32_t((r >> 2) * 1024 + ((r & 3) * 16 + (k ^ r)) * 16);
+  }
+  const bool mover = wu < NQ;
+  auto issue = [&](int g) {
+    if (mover) {
+      const uint32_t sb = lds_addr(&ring[g % RG][wu][0]);
+      const uint32_t base = uint32_t(g) * 16u * wrowbytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16_nt(wsrd, sb + uint32_t(i) * 1024u, vq[i] + base);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < RG - 1; ++j) issue(j);
+
+  // Tile w of the normalised rows over block q (rows past M read as zero).  Issued after
+  // the DMA loads: the waits the compiler places for these then also cover the DMA.
+  const int tok = 16 * wu + (lane & 15);
+  const bool live = 16 * wu < a.M;
+  const rsrc_t xr = make_rsrc(a.xhat, (uint64_t)a.M * wrowbytes);
+  uint4 xf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    xf[s] = bload16(xr, (live && tok < a.M) ? uint32_t(tok) * wrowbytes +
+                            uint32_t(q * kWideBlock + 32 * s + 8 * (lane >> 4)) * 2u
+                                            : kOutOfRange, 0);
+  // Plane q, rows [r0, r1): stores past the chunk are dropped.
+  const rsrc_t pr = make_rsrc(a.planes + ((size_t)q * V + r0) * mp, (uint64_t)(r1 - r0) * mp * 4u);
+  const uint32_t pofs = (uint32_t(4 * (lane >> 4)) * uint32_t(mp) + uint32_t(tok)) * 4u;
+
+  for (int g = 0; g < ng; ++g) {
+    // this wave's quarter of group g has landed (RG - 2 later groups of DMA outstanding)
+    wait_vmcnt<4 * (RG - 2)>();
+    __syncthreads();  // every quarter of group g is in LDS; group g - 1's slot is free
+    issue(g + RG - 1);
+    if (live) {
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+      const char* sb = reinterpret_cast<const char*>(&ring[g % RG][0][0]);
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint4 fw = *reinterpret_cast<const uint4*>(sb + c * 4096 + rdo[t]);
+          acc = mfma_step<JSV_BF16>(fw, xf[4 * c + t], acc);
+        }
+      }
+      const uint32_t go = uint32_t(g) * 16u * uint32_t(mp) * 4u + pofs;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bstore4f(acc[i], pr, go + uint32_t(i) * uint32_t(mp) * 4u);
+    }
+  }
+  wait_vmcnt<0>();  // no DMA write into LDS may outlive the workgroup
+}
+
+// Part 3: logits and partial statistics, 1024 threads.  Workgroup wg takes the vocabulary
+// columns [V wg / P, V (wg + 1) / P) in tiles of 64.  Per tile every thread issues all its
+// loads at once (its share of the S plane tiles and, for a draft row, its draft logits),
+// the planes are summed in float64 in block order into an LDS tile [column][row], and
+// the four threads of row m take the columns u, u + 4, ..., u + 60: they write the
+// logits and fold them (and the draft logits) into running statistics, merged into the
+// row's partial record at the end.
+constexpr int kWideCombineThreads = 1024;
+constexpr int kWideMaxS = 5;  // blocks of d the combine kernel holds per tile
+__global__ __launch_bounds__(kWideCombineThreads) void wide_stats_kernel(WideArgs a) {
+  constexpr int TC = 64;
+  constexpr int PER = (TC * kWideMaxRows / 4 + kWideCombineThreads - 1) / kWideCombineThreads;
+  __shared__ float zt[TC][kWideMaxRows + 1];
+  const int tid = threadIdx.x;
+  const int S = a.pl.S, mp = a.pl.mp, P = a.pl.ncomb, M = a.M;
+  const int wg = blockIdx.x;
+  const int64_t V = a.V;
+  const int64_t c0 = V * wg / P, c1 = V * (wg + 1) / P;
+  const int m = tid >> 2, u = tid & 3;
+  const bool rowok = m < M;
+  const bool soft = a.T > 0.f;
+  const float c = a.c;
+  int grow = -1;
+  if (rowok && a.want_q) {
+    const int b = m / (a.K + 1), i = m - b * (a.K + 1);
+    if (i < a.K) grow = b * a.K + i;
+  }
+  const rsrc_t gr = make_rsrc(a.G, a.want_q ? (uint64_t)a.B * a.K * (uint64_t)V * 4u : 0u);
+  const rsrc_t lr = make_rsrc(a.logits, (uint64_t)M * (uint64_t)V * 4u);
+  rsrc_t pr[kWideMaxS];
+#pragma unroll
+  for (int qq = 0; qq < kWideMaxS; ++qq)
+    pr[qq] = make_rsrc(a.planes + (size_t)(qq < S ? qq : 0) * V * mp, qq < S ? (uint64_t)V * mp * 4u : 0u);
+  const int f4 = TC * mp / 4;  // float4 groups of a plane tile
+  Stat st;
+  stat_init(st);
+  for (int64_t v0 = c0; v0 < c1; v0 += TC) {
+    float gv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t v = v0 + 4 * e + u;
+      gv[e] = bload4f(gr, (grow >= 0 && v < c1) ? uint32_t((int64_t)grow * V + v) * 4u : kOutOfRange);
+    }
+    uint4 x[PER][kWideMaxS];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int jj = tid + j * kWideCombineThreads;
+      const uint32_t off = jj < f4 ? uint32_t(v0 * mp) * 4u + uint32_t(jj) * 16u : kOutOfRange;
+#pragma unroll
+      for (int qq = 0; qq < kWideMaxS; ++qq) x[j][qq] = bload16(pr[qq], off, 0);
+    }
+    __syncthreads();  // the previous tile's readers are done with zt
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int jj = tid + j * kWideCombineThreads;
+      if (jj < f4) {
+        double sum[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int qq = 0; qq < kWideMaxS; ++qq) {  // planes past S read as zero
+          sum[0] += double(__uint_as_float(x[j][qq].x));
+          sum[1] += double(__uint_as_float(x[j][qq].y));
+          sum[2] += double(__uint_as_float(x[j][qq].z));
+          sum[3] += double(__uint_as_float(x[j][qq].w));
+        }
+        const int e = 4 * jj, col = e / mp, row = e - col * mp;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) zt[col][row + k] = float(sum[k]);
+      }
+    }
+    __syncthreads();
+    if (rowok) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int col = 4 * e + u;
+        const int64_t v = v0 + col;
+        const bool vok = v < c1;
+        const float z = zt[col][m];
+        bstore4f(z, lr, vok ? uint32_t((int64_t)m * V + v) * 4u : kOutOfRange);
+        const bool fin = fabsf(z) <= FLT_MAX;
+        if (vok && !fin) st.flags |= JSV_FLAG_INVALID;
+        const float ze = (vok && fin) ? z : -INFINITY;
+        if (ze > st.m) { st.top2 = st.m; st.idx = int(v); } else { st.top2 = fmaxf(st.top2, ze); }
+        if (soft) fold(st.m, st.s, ze, c); else st.m = fmaxf(st.m, ze);
+        if (grow >= 0) {
+          const float gq = gv[e];
+          const bool qf = fabsf(gq) <= FLT_MAX;
+          if (vok && !qf) st.flags |= JSV_FLAG_INVALID;
+          fold(st.mq, st.sq, (vok && qf) ? gq : -INFINITY, c);
+        }
+      }
+    }
+  }
+  // the four threads of a row (consecutive lanes) merge in a fixed order
+  stat_merge(st, stat_dpp<0xB1>(st), c, soft);
+  stat_merge(st, stat_dpp<0x4E>(st), c, soft);
+  if (rowok && u == 0) {
+    RowStat rs;
+    rs.s = st.s; rs.sq = st.sq; rs.m = st.m; rs.top2 = st.top2; rs.mq = st.mq;
+    rs.idxf = (uint32_t(st.idx) & kIdxMask) | (st.flags ? kBadBit : 0u);
+    a.partial[(size_t)m * P + wg] = rs;
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Finalize, part 1 (rowstat_kernel): grid (tasks, B) of one-wave workgroups, so that
 // the reads spread over the chip.  Task i < K (T > 0 only): the float64 logit of draft
 // row i at its draft token, from the normalised row and W[d_i], so that alpha and
@@ -1694,6 +1920,24 @@ hipError_t launch_stats(int dtype, int nks, int grid, const StatsArgs& a, hipStr
   if (dtype == JSV_FP8) return dispatch_rows<JSV_FP8>(nks, grid, a, stream);
   return dtype == JSV_BF16 ? dispatch_rows<JSV_BF16>(nks, grid, a, stream)
                            : dispatch_rows<JSV_F32>(nks, grid, a, stream);
+}
+
+hipError_t launch_wide(const WideArgs& a, hipStream_t stream) {
+  if (!wide_eligible(JSV_BF16, a.d, a.M) || a.pl.mp % 16 != 0 || a.pl.mp < a.M ||
+      a.pl.mp > 16 * a.pl.nw || a.pl.mp > kWideMaxRows ||
+      a.pl.S * kWideBlock != a.d || a.pl.nchunk < 1 || a.pl.ncomb < 1 || a.pl.ncomb > kMaxGrid)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(xhat_kernel, dim3(a.M), dim3(kSliceThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.pl.nw == 8)
+    hipLaunchKernelGGL(wide_kernel<8>, dim3(a.pl.nchunk * a.pl.S), dim3(8 * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL(wide_kernel<9>, dim3(a.pl.nchunk * a.pl.S), dim3(9 * kWave), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(wide_stats_kernel, dim3(a.pl.ncomb), dim3(kWideCombineThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_rowstat(const FinalArgs& a, hipStream_t stream) {

@@ -198,6 +198,25 @@ def test_verify_ragged_vocab_staged_head(dev):
     assert st["exact"] >= 6
 
 
+def test_verify_split_d_ragged(dev):
+    """More rows than one pass holds, on a ragged vocabulary: the LM head splits d into
+    blocks of 1024 columns (two here) and sums their partial products.  B = 3, K = 32
+    (99 rows, seven tiles), V = 5003, both temperatures and both proposals."""
+    head = synth.random_head(5003, 2048, synth.BF16, seed=41)
+    case = Case(head, dev)
+    ws = jsv.new_workspace(case.gpu, 3, 32)
+    st = new_stats()
+    for T, mode in ((0.0, SOFT), (1.0, SOFT), (1.0, POINT)):
+        for seed in range(2):
+            say(f"split-d V=5003 d=2048 B=3 K=32 T={T} mode={mode} seed={seed}")
+            blk = synth.make_block(head, 3, 32, 0.3, T, seed=70 + seed)
+            got, ref = run_verify(case, blk, T, mode, seed, 4, ws)
+            compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+            compare_logits(got["logits"], ref["logits"], st)
+    say(f"  {st}")
+    assert st["exact"] >= 12
+
+
 def test_verify_d5120(dev):
     head = synth.head_for(synth.CONFIGS["d5120_k16_b1"])
     case = Case(head, dev, f64_weight=True)
