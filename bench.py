@@ -87,13 +87,42 @@ def _counter_means(csv_path, name_prefix):
     return sum(vals) / len(vals), len(vals)
 
 
+# The LM-head kernels of jsv_verify_stats: the fused kernel, or for more rows than one pass
+# holds (bf16) the split-d kernels.
+LMHEAD_KERNELS = ("void jsv::stats_kernel", "jsv::xhat_kernel", "void jsv::wide_kernel",
+                  "void jsv::wide_stats_kernel")
+
+
+def wide_path(cfg):
+    """True when verification of this workload takes the split-d LM head (bf16, 34..144
+    rows, d a multiple of 1024 up to 5120)."""
+    M = cfg.batch * (cfg.K + 1)
+    return cfg.dtype == "bf16" and 33 < M <= 144 and cfg.hidden % 1024 == 0 and cfg.hidden <= 5120
+
+
+def _lmhead_means(csv_path):
+    """Sum over the LM-head kernels present of their mean counter value per dispatch."""
+    total, n, names = 0.0, 0, []
+    for k in LMHEAD_KERNELS:
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+                if r["Kernel_Name"].startswith(k)]
+        if vals:
+            total += sum(vals) / len(vals)
+            n = max(n, len(vals))
+            names.append(k.replace("void ", ""))
+    if not names:
+        raise SystemExit(f"no LM-head dispatch in {csv_path}")
+    return total, n, names
+
+
 def pmc_summary(pmc_dir, config):
     """Counter runs -> traffic summary.  FETCH_SIZE and WRITE_SIZE are KiB per dispatch;
-    each is scaled by the factor that makes the 1 GiB copy read and write 1 GiB."""
+    each is scaled by the factor that makes the 1 GiB copy read and write 1 GiB.  With the
+    split-d LM head the three kernels of one call are added."""
     d = Path(pmc_dir)
-    kname = "void jsv::stats_kernel"
-    f_kib, nf = _counter_means(d / "bench_FETCH_SIZE" / "run_counter_collection.csv", kname)
-    w_kib, nw = _counter_means(d / "bench_WRITE_SIZE" / "run_counter_collection.csv", kname)
+    f_kib, nf, names = _lmhead_means(d / "bench_FETCH_SIZE" / "run_counter_collection.csv")
+    w_kib, nw, _ = _lmhead_means(d / "bench_WRITE_SIZE" / "run_counter_collection.csv")
+    kname = " + ".join(names)
     cf_kib, _ = _counter_means(d / "copy_FETCH_SIZE" / "run_counter_collection.csv", "__amd_rocclr_copyBuffer")
     cw_kib, _ = _counter_means(d / "copy_WRITE_SIZE" / "run_counter_collection.csv", "__amd_rocclr_copyBuffer")
     sf = COPY_PROBE_BYTES / (cf_kib * 1024.0)
@@ -221,7 +250,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(args.config) if (T > 0 and not args.point) else None,
-                     "kernel": "stats_kernel (fused RMSNorm + LM head + softmax statistics)",
+                     "kernel": ("xhat_kernel + wide_kernel + wide_stats_kernel (split-d RMSNorm + LM head "
+                                "+ softmax statistics)" if wide_path(cfg) else
+                                "stats_kernel (fused RMSNorm + LM head + softmax statistics)"),
                      "algorithmic_bytes": abytes},
         "mfma": {"achieved": round(lmhead_flops(cfg) / (k1_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                  "unit": "TFLOP/s", "frac": round(lmhead_flops(cfg) / (k1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -105,7 +105,7 @@ struct WidePlan {
   int mp;      // rows of a partial plane: M rounded up to whole tiles
   int S;       // blocks of d
   int nchunk;  // vocabulary chunks of the product kernel
-  int ncomb;   // workgroups of the combine kernel (= partial statistics per row)
+  int ncomb;   // column chunks of the combine kernel (= partial statistics per row)
 };
 inline WidePlan plan_wide(int64_t V, int64_t d, int M, int cus) {
   WidePlan p{};
@@ -117,7 +117,9 @@ inline WidePlan plan_wide(int64_t V, int64_t d, int M, int cus) {
   if (nc < 1) nc = 1;
   if (nc > ngroups) nc = ngroups;
   p.nchunk = int(nc);
-  int64_t cb = cus < kMaxGrid ? cus : kMaxGrid;
+  // combine: (column chunks) x (row groups) workgroups of 256 threads, about four per CU
+  int64_t cb = (4 * int64_t(cus) + (M + 15) / 16 - 1) / ((M + 15) / 16);
+  if (cb > kMaxGrid) cb = kMaxGrid;
   const int64_t ntiles = (V + 63) / 64;
   if (cb > ntiles) cb = ntiles;
   p.ncomb = int(cb > 0 ? cb : 1);

@@ -941,8 +941,8 @@ __global__ __launch_bounds__(kSliceThreads) void xhat_kernel(WideArgs a) {
 // rows x 1024 columns, 32 KB) from LDS.  The group is staged by DMA in eight quarters of
 // 4 k-steps, wave w < 8 moving quarter w in the layout of the LM-head kernel (4 rows x
 // 256 contiguous bytes per load, row-XOR swizzle), three groups ahead.  The products go to
-// plane q in [vocabulary][row] order straight from the accumulators: the waves of a group
-// fill whole rows of the plane between them.
+// plane q in [row group][vocabulary][16 rows] order straight from the accumulators: the
+// four stores of a wave fill one contiguous kilobyte.
 template <int NW>
 __global__ __launch_bounds__(NW * kWave) void wide_kernel(WideArgs a) {
   constexpr int NQ = kWideBlock / 128;  // quarters of a group (4 k-steps of 32 columns)
@@ -993,9 +993,12 @@ __global__ __launch_bounds__(NW * kWave) void wide_kernel(WideArgs a) {
     xf[s] = bload16(xr, (live && tok < a.M) ? uint32_t(tok) * wrowbytes +
                             uint32_t(q * kWideBlock + 32 * s + 8 * (lane >> 4)) * 2u
                                             : kOutOfRange, 0);
-  // Plane q, rows [r0, r1): stores past the chunk are dropped.
-  const rsrc_t pr = make_rsrc(a.planes + ((size_t)q * V + r0) * mp, (uint64_t)(r1 - r0) * mp * 4u);
-  const uint32_t pofs = (uint32_t(4 * (lane >> 4)) * uint32_t(mp) + uint32_t(tok)) * 4u;
+  // Plane q, row group wu, vocabulary rows [r0, r1) ([q][group][V][16] layout): stores
+  // past the chunk are dropped.
+  const int ngr = mp / 16;
+  const rsrc_t pr = make_rsrc(a.planes + (((size_t)q * ngr + (live ? wu : 0)) * V + r0) * 16,
+                              live ? (uint64_t)(r1 - r0) * 64u : 0u);
+  const uint32_t pofs = (uint32_t(4 * (lane >> 4)) * 16u + uint32_t(lane & 15)) * 4u;
 
   for (int g = 0; g < ng; ++g) {
     // this wave's quarter of group g has landed (RG - 2 later groups of DMA outstanding)
@@ -1013,33 +1016,32 @@ __global__ __launch_bounds__(NW * kWave) void wide_kernel(WideArgs a) {
           acc = mfma_step<JSV_BF16>(fw, xf[4 * c + t], acc);
         }
       }
-      const uint32_t go = uint32_t(g) * 16u * uint32_t(mp) * 4u + pofs;
+      const uint32_t go = uint32_t(g) * 1024u + pofs;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bstore4f(acc[i], pr, go + uint32_t(i) * uint32_t(mp) * 4u);
+      for (int i = 0; i < 4; ++i) bstore4f(acc[i], pr, go + uint32_t(i) * 64u);
     }
   }
   wait_vmcnt<0>();  // no DMA write into LDS may outlive the workgroup
 }
 
-// Part 3: logits and partial statistics, 1024 threads.  Workgroup wg takes the vocabulary
-// columns [V wg / P, V (wg + 1) / P) in tiles of 64.  Per tile every thread issues all its
-// loads at once (its share of the S plane tiles and, for a draft row, its draft logits),
-// the planes are summed in float64 in block order into an LDS tile [column][row], and
-// the four threads of row m take the columns u, u + 4, ..., u + 60: they write the
-// logits and fold them (and the draft logits) into running statistics, merged into the
-// row's partial record at the end.
-constexpr int kWideCombineThreads = 1024;
-constexpr int kWideMaxS = 5;  // blocks of d the combine kernel holds per tile
+// Part 3: logits and partial statistics.  Workgroup (wg, group rg) of 256 threads takes the
+// 16 rows of row group rg over the vocabulary columns [V wg / P, V (wg + 1) / P), in tiles
+// of 64: the S plane tiles (4 KB each, contiguous) are summed in float64 in block order
+// into an LDS tile [column][row], then the 16 threads of row m take the columns
+// u, u + 16, u + 32, u + 48: they write the logits and fold them (and the draft logits)
+// into running statistics, merged over the 16 lanes into the row's partial record at the
+// end.  A workgroup touches 16 rows of the logits and draft logits at a time.
+constexpr int kWideCombineThreads = 256;
+template <int NS>  // blocks of d (= a.pl.S)
 __global__ __launch_bounds__(kWideCombineThreads) void wide_stats_kernel(WideArgs a) {
   constexpr int TC = 64;
-  constexpr int PER = (TC * kWideMaxRows / 4 + kWideCombineThreads - 1) / kWideCombineThreads;
-  __shared__ float zt[TC][kWideMaxRows + 1];
+  __shared__ float zt[TC][17];
   const int tid = threadIdx.x;
-  const int S = a.pl.S, mp = a.pl.mp, P = a.pl.ncomb, M = a.M;
-  const int wg = blockIdx.x;
+  const int ngr = a.pl.mp / 16, P = a.pl.ncomb, M = a.M;
+  const int wg = blockIdx.x, rg = blockIdx.y;
   const int64_t V = a.V;
   const int64_t c0 = V * wg / P, c1 = V * (wg + 1) / P;
-  const int m = tid >> 2, u = tid & 3;
+  const int ml = tid >> 4, u = tid & 15, m = 16 * rg + ml;
   const bool rowok = m < M;
   const bool soft = a.T > 0.f;
   const float c = a.c;
@@ -1050,54 +1052,44 @@ __global__ __launch_bounds__(kWideCombineThreads) void wide_stats_kernel(WideArg
   }
   const rsrc_t gr = make_rsrc(a.G, a.want_q ? (uint64_t)a.B * a.K * (uint64_t)V * 4u : 0u);
   const rsrc_t lr = make_rsrc(a.logits, (uint64_t)M * (uint64_t)V * 4u);
-  rsrc_t pr[kWideMaxS];
+  rsrc_t pr[NS];
 #pragma unroll
-  for (int qq = 0; qq < kWideMaxS; ++qq)
-    pr[qq] = make_rsrc(a.planes + (size_t)(qq < S ? qq : 0) * V * mp, qq < S ? (uint64_t)V * mp * 4u : 0u);
-  const int f4 = TC * mp / 4;  // float4 groups of a plane tile
+  for (int qq = 0; qq < NS; ++qq)
+    pr[qq] = make_rsrc(a.planes + ((size_t)qq * ngr + rg) * V * 16, (uint64_t)V * 64u);
   Stat st;
   stat_init(st);
   for (int64_t v0 = c0; v0 < c1; v0 += TC) {
-    float gv[16];
+    float gv[TC / 16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t v = v0 + 4 * e + u;
+    for (int e = 0; e < TC / 16; ++e) {
+      const int64_t v = v0 + 16 * e + u;
       gv[e] = bload4f(gr, (grow >= 0 && v < c1) ? uint32_t((int64_t)grow * V + v) * 4u : kOutOfRange);
     }
-    uint4 x[PER][kWideMaxS];
+    uint4 x[NS];
+    const uint32_t off = uint32_t(v0) * 64u + uint32_t(tid) * 16u;  // 64 columns x 16 rows
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int jj = tid + j * kWideCombineThreads;
-      const uint32_t off = jj < f4 ? uint32_t(v0 * mp) * 4u + uint32_t(jj) * 16u : kOutOfRange;
+    for (int qq = 0; qq < NS; ++qq) x[qq] = bload16(pr[qq], off, 0);
+    double sum[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int qq = 0; qq < kWideMaxS; ++qq) x[j][qq] = bload16(pr[qq], off, 0);
+    for (int qq = 0; qq < NS; ++qq) {
+      sum[0] += double(__uint_as_float(x[qq].x));
+      sum[1] += double(__uint_as_float(x[qq].y));
+      sum[2] += double(__uint_as_float(x[qq].z));
+      sum[3] += double(__uint_as_float(x[qq].w));
     }
-    __syncthreads();  // the previous tile's readers are done with zt
+    {
+      const int e = 4 * tid, col = e >> 4, row = e & 15;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int jj = tid + j * kWideCombineThreads;
-      if (jj < f4) {
-        double sum[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-        for (int qq = 0; qq < kWideMaxS; ++qq) {  // planes past S read as zero
-          sum[0] += double(__uint_as_float(x[j][qq].x));
-          sum[1] += double(__uint_as_float(x[j][qq].y));
-          sum[2] += double(__uint_as_float(x[j][qq].z));
-          sum[3] += double(__uint_as_float(x[j][qq].w));
-        }
-        const int e = 4 * jj, col = e / mp, row = e - col * mp;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) zt[col][row + k] = float(sum[k]);
-      }
+      for (int k = 0; k < 4; ++k) zt[col][row + k] = float(sum[k]);
     }
-    __syncthreads();
+    __syncthreads();  // zt holds tile v0
     if (rowok) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int col = 4 * e + u;
+      for (int e = 0; e < TC / 16; ++e) {
+        const int col = 16 * e + u;
         const int64_t v = v0 + col;
         const bool vok = v < c1;
-        const float z = zt[col][m];
+        const float z = zt[col][ml];
         bstore4f(z, lr, vok ? uint32_t((int64_t)m * V + v) * 4u : kOutOfRange);
         const bool fin = fabsf(z) <= FLT_MAX;
         if (vok && !fin) st.flags |= JSV_FLAG_INVALID;
@@ -1112,10 +1104,9 @@ __global__ __launch_bounds__(kWideCombineThreads) void wide_stats_kernel(WideArg
         }
       }
     }
+    __syncthreads();  // the readers are done with zt
   }
-  // the four threads of a row (consecutive lanes) merge in a fixed order
-  stat_merge(st, stat_dpp<0xB1>(st), c, soft);
-  stat_merge(st, stat_dpp<0x4E>(st), c, soft);
+  stat_row_reduce(st, c, soft);  // the 16 lanes of a row, in a fixed order
   if (rowok && u == 0) {
     RowStat rs;
     rs.s = st.s; rs.sq = st.sq; rs.m = st.m; rs.top2 = st.top2; rs.mq = st.mq;
@@ -1936,7 +1927,16 @@ hipError_t launch_wide(const WideArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(wide_kernel<9>, dim3(a.pl.nchunk * a.pl.S), dim3(9 * kWave), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(wide_stats_kernel, dim3(a.pl.ncomb), dim3(kWideCombineThreads), 0, stream, a);
+  switch (a.pl.S) {
+#define JSV_WIDE_S(n)                                                                            \
+  case n:                                                                                        \
+    hipLaunchKernelGGL(wide_stats_kernel<n>, dim3(a.pl.ncomb, a.pl.mp / 16), dim3(kWideCombineThreads), 0, \
+                       stream, a);                                                              \
+    break;
+    JSV_WIDE_S(1) JSV_WIDE_S(2) JSV_WIDE_S(3) JSV_WIDE_S(4) JSV_WIDE_S(5)
+#undef JSV_WIDE_S
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
