@@ -55,3 +55,13 @@ def test_traffic_is_dropped_when_kernel_sources_change(monkeypatch):
         assert a <= t <= 1.1 * a
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
     assert bench.measured_traffic("qwen8b_k16") is None
+
+
+def test_split_d_workloads_are_labelled():
+    """The bench names the split-d kernels for the workloads that take them (bf16, 34..144
+    rows) and the fused kernel otherwise."""
+    assert bench.wide_path(synth.CONFIGS["qwen8b_k32_b4"])
+    assert bench.wide_path(synth.CONFIGS["d5120_k32_b2"])
+    assert not bench.wide_path(synth.CONFIGS["qwen8b_k16"])
+    assert not bench.wide_path(synth.CONFIGS["qwen8b_k16_fp8"])
+    assert not bench.wide_path(synth.CONFIGS["tiny"])

@@ -59,6 +59,27 @@ def test_workspace_bytes(lib):
         assert lib.jsv_workspace_bytes(ctypes.byref(bad), 1, 16, 8) == 0
 
 
+def test_workspace_holds_the_split_d_planes(lib):
+    """34..144 rows on a bf16 head with d a multiple of 1024 (up to 5120) take the split-d
+    LM head: the workspace then also holds the normalised rows and the fp32 partial-product
+    planes (blocks x V x rows rounded up to 16).  Other heads and row counts do not."""
+    V = 151936
+    bf = head(vocab=V, hidden=4096)
+    n_wide = lib.jsv_workspace_bytes(ctypes.byref(bf), 4, 32, 8)       # 132 rows
+    planes = 4 * V * 144 * 4
+    assert n_wide >= planes + 132 * V * 4 + 132 * 4096 * 2
+    fp8 = head(vocab=V, hidden=4096, dtype=J.JSV_FP8)
+    n_fp8 = lib.jsv_workspace_bytes(ctypes.byref(fp8), 4, 32, 8)
+    assert n_fp8 < planes                                               # row passes, no planes
+    # one pass of rows (B (K + 1) <= 33) never needs the planes
+    assert lib.jsv_workspace_bytes(ctypes.byref(bf), 1, 32, 8) < planes
+    # d = 3072 is three blocks, d = 5120 five
+    d3 = head(vocab=V, hidden=3072)
+    assert lib.jsv_workspace_bytes(ctypes.byref(d3), 2, 32, 8) >= 3 * V * 80 * 4
+    d5 = head(vocab=V, hidden=5120)
+    assert lib.jsv_workspace_bytes(ctypes.byref(d5), 4, 32, 8) >= 5 * V * 144 * 4
+
+
 def _verify(lib, h=None, **kw):
     a = dict(hidden=FAKE, drafts=FAKE, dl=FAKE, B=1, K=16, T=1.0, mode=0, seed=0, offset=0,
              nacc=FAKE, comm=FAKE, flags=0, lout=0, ws=FAKE, wsb=1 << 40, stream=0)
