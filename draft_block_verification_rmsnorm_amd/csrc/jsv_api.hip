@@ -85,6 +85,7 @@ jsv_status run_stats(const jsv_lm_head* head, int nks, const void* hidden, int M
     w.T = T;
     w.c = T > 0.f ? kLog2e / T : 0.f;
     w.want_q = (mode == JSV_PROPOSAL_SOFTMAX && T > 0.f && G != nullptr) ? 1 : 0;
+    w.quad = ((head->vocab & 3) == 0 && aligned16(logits) && (G == nullptr || aligned16(G))) ? 1 : 0;
     w.partial = partial;
     return launch_wide(w, stream) == hipSuccess ? JSV_OK : JSV_EHIP;
   }

@@ -143,7 +143,7 @@ inline WsLayout ws_layout(int64_t V, int B, int K, int top_n, int64_t d, int dty
   const bool wide = wide_eligible(dtype, d, int(M));
   const WidePlan wp = plan_wide(V, d > 0 ? d : kWideBlock, int(M), 1);
   L.xhat = off;     off = align256(off + (wide ? M * size_t(d) * 2 : 0));
-  L.planes = off;   off = align256(off + (wide ? size_t(wp.S) * size_t(V) * size_t(wp.mp) * 4 : 0));
+  L.planes = off;   off = align256(off + (wide ? size_t(wp.S) * size_t((V + 3) & ~int64_t(3)) * size_t(wp.mp) * 4 : 0));
   const size_t zs_sample = size_t(B) * size_t(sample_slices(V)) * 2 * sizeof(double);
   const size_t zs_score = M * size_t(score_slices(V)) * sizeof(double);
   L.zs = off;       off = align256(off + (zs_sample > zs_score ? zs_sample : zs_score));
@@ -275,13 +275,14 @@ struct WideArgs {
   float eps;
   WidePlan pl;
   uint16_t* xhat;         // [M][d] normalised rows (workspace)
-  float* planes;          // [S][V][mp] partial products (workspace)
+  float* planes;          // [S][mp / 16][16][V rounded up to 4] partial products (workspace)
   float* rnorm;           // [M]
   float* logits;          // [M][V]
   const float* G;         // [B][K][V] draft logits, or null
   int B, K;
   float T, c;             // temperature and log2(e) / T
   int want_q;
+  int quad;               // V % 4 == 0 and logits, G 16-byte aligned: 16-byte accesses
   RowStat* partial;       // [M][ncomb]
 };
 hipError_t launch_wide(const WideArgs& a, hipStream_t stream);

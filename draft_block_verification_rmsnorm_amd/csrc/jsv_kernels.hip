@@ -81,6 +81,9 @@ __device__ inline float bload4f(rsrc_t r, uint32_t voff) {
 __device__ inline void bstore4f(float x, rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, 0, 0);
 }
+__device__ inline void bstore16(const uint4& x, rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, r, (int)voff, 0, 0);
+}
 // Same, marked non-temporal (streaming data the writer does not read again).
 __device__ inline void bstore4f_nt(float x, rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, 0, 2);
@@ -941,8 +944,8 @@ __global__ __launch_bounds__(kSliceThreads) void xhat_kernel(WideArgs a) {
 // rows x 1024 columns, 32 KB) from LDS.  The group is staged by DMA in eight quarters of
 // 4 k-steps, wave w < 8 moving quarter w in the layout of the LM-head kernel (4 rows x
 // 256 contiguous bytes per load, row-XOR swizzle), three groups ahead.  The products go to
-// plane q in [row group][vocabulary][16 rows] order straight from the accumulators: the
-// four stores of a wave fill one contiguous kilobyte.
+// plane q in [row group][row][vocabulary] order straight from the accumulators, one
+// 16-byte store per lane (its four values are consecutive vocabulary rows of one row).
 template <int NW>
 __global__ __launch_bounds__(NW * kWave) void wide_kernel(WideArgs a) {
   constexpr int NQ = kWideBlock / 128;  // quarters of a group (4 k-steps of 32 columns)
@@ -953,8 +956,10 @@ __global__ __launch_bounds__(NW * kWave) void wide_kernel(WideArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int S = a.pl.S, P = a.pl.nchunk, mp = a.pl.mp;
   const int q = blockIdx.x % S, chunk = blockIdx.x / S;
-  const int64_t V = a.V;
-  const int64_t r0 = V * chunk / P, r1 = V * (chunk + 1) / P;
+  const int64_t V = a.V, Vp = (V + 3) & ~int64_t(3);
+  const int64_t ngroups = (V + 15) >> 4;  // chunks start on whole 16-row groups
+  const int64_t r0 = 16 * (ngroups * chunk / P);
+  const int64_t r1 = min(V, 16 * (ngroups * (chunk + 1) / P));
   const int ng = int((r1 - r0 + 15) >> 4);
   const uint32_t wrowbytes = uint32_t(a.d) * 2u;
 
@@ -993,12 +998,13 @@ __global__ __launch_bounds__(NW * kWave) void wide_kernel(WideArgs a) {
     xf[s] = bload16(xr, (live && tok < a.M) ? uint32_t(tok) * wrowbytes +
                             uint32_t(q * kWideBlock + 32 * s + 8 * (lane >> 4)) * 2u
                                             : kOutOfRange, 0);
-  // Plane q, row group wu, vocabulary rows [r0, r1) ([q][group][V][16] layout): stores
-  // past the chunk are dropped.
+  // Plane q, row group wu ([q][group][16 rows][Vp] layout, Vp = V rounded up to 4): lane
+  // l holds the products of vocabulary rows v .. v + 3 (v = 16 g + 4 (l / 16) past r0) for
+  // row l mod 16, stored as one 16-byte write; quads past Vp are not written.
   const int ngr = mp / 16;
-  const rsrc_t pr = make_rsrc(a.planes + (((size_t)q * ngr + (live ? wu : 0)) * V + r0) * 16,
-                              live ? (uint64_t)(r1 - r0) * 64u : 0u);
-  const uint32_t pofs = (uint32_t(4 * (lane >> 4)) * 16u + uint32_t(lane & 15)) * 4u;
+  const rsrc_t pr = make_rsrc(a.planes + ((size_t)q * ngr + (live ? wu : 0)) * 16 * Vp,
+                              live ? (uint64_t)16 * Vp * 4u : 0u);
+  const uint32_t prow = uint32_t(lane & 15) * uint32_t(Vp);
 
   for (int g = 0; g < ng; ++g) {
     // this wave's quarter of group g has landed (RG - 2 later groups of DMA outstanding)
@@ -1016,21 +1022,22 @@ __global__ __launch_bounds__(NW * kWave) void wide_kernel(WideArgs a) {
           acc = mfma_step<JSV_BF16>(fw, xf[4 * c + t], acc);
         }
       }
-      const uint32_t go = uint32_t(g) * 1024u + pofs;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bstore4f(acc[i], pr, go + uint32_t(i) * 64u);
+      const int64_t v = r0 + 16 * g + 4 * (lane >> 4);
+      bstore16(make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                          __float_as_uint(acc[3])),
+               pr, v < Vp ? (prow + uint32_t(v)) * 4u : kOutOfRange);
     }
   }
   wait_vmcnt<0>();  // no DMA write into LDS may outlive the workgroup
 }
 
 // Part 3: logits and partial statistics.  Workgroup (wg, group rg) of 256 threads takes the
-// 16 rows of row group rg over the vocabulary columns [V wg / P, V (wg + 1) / P), in tiles
-// of 64: the S plane tiles (4 KB each, contiguous) are summed in float64 in block order
-// into an LDS tile [column][row], then the 16 threads of row m take the columns
-// u, u + 16, u + 32, u + 48: they write the logits and fold them (and the draft logits)
-// into running statistics, merged over the 16 lanes into the row's partial record at the
-// end.  A workgroup touches 16 rows of the logits and draft logits at a time.
+// 16 rows of row group rg over its share of the vocabulary (whole tiles of 64 columns):
+// per tile the S plane tiles (16 rows x 256 B each) are summed in float64 in block order
+// into an LDS tile [column][row], then the 16 threads of row m take four consecutive
+// columns each: they write the logits and fold them (and the draft logits) into running
+// statistics, merged over the 16 lanes into the row's partial record at the end.  With V
+// a multiple of 4 every logit store and draft-logit load is one 16-byte access.
 constexpr int kWideCombineThreads = 256;
 template <int NS>  // blocks of d (= a.pl.S)
 __global__ __launch_bounds__(kWideCombineThreads) void wide_stats_kernel(WideArgs a) {
@@ -1039,11 +1046,13 @@ __global__ __launch_bounds__(kWideCombineThreads) void wide_stats_kernel(WideArg
   const int tid = threadIdx.x;
   const int ngr = a.pl.mp / 16, P = a.pl.ncomb, M = a.M;
   const int wg = blockIdx.x, rg = blockIdx.y;
-  const int64_t V = a.V;
-  const int64_t c0 = V * wg / P, c1 = V * (wg + 1) / P;
+  const int64_t V = a.V, Vp = (V + 3) & ~int64_t(3);
+  const int64_t ntiles = (V + TC - 1) / TC;
+  const int64_t c0 = TC * (ntiles * wg / P), c1 = min(V, TC * (ntiles * (wg + 1) / P));
   const int ml = tid >> 4, u = tid & 15, m = 16 * rg + ml;
   const bool rowok = m < M;
   const bool soft = a.T > 0.f;
+  const bool quad = a.quad != 0;  // rows of the logits and draft logits are 16-byte aligned
   const float c = a.c;
   int grow = -1;
   if (rowok && a.want_q) {
@@ -1055,18 +1064,25 @@ __global__ __launch_bounds__(kWideCombineThreads) void wide_stats_kernel(WideArg
   rsrc_t pr[NS];
 #pragma unroll
   for (int qq = 0; qq < NS; ++qq)
-    pr[qq] = make_rsrc(a.planes + ((size_t)qq * ngr + rg) * V * 16, (uint64_t)V * 64u);
+    pr[qq] = make_rsrc(a.planes + ((size_t)qq * ngr + rg) * 16 * Vp, (uint64_t)16 * Vp * 4u);
+  // plane element of this thread in the tile: row tid / 16, columns 4 (tid mod 16) .. + 3
+  const uint32_t prow = uint32_t(tid >> 4) * uint32_t(Vp);
   Stat st;
   stat_init(st);
   for (int64_t v0 = c0; v0 < c1; v0 += TC) {
-    float gv[TC / 16];
+    const int64_t vq = v0 + 4 * u;  // this thread's four columns in the fold
+    float gv[4];
+    if (quad) {
+      const uint4 g4 = bload16(gr, (grow >= 0 && vq < c1) ? uint32_t((int64_t)grow * V + vq) * 4u : kOutOfRange, 0);
+      gv[0] = __uint_as_float(g4.x); gv[1] = __uint_as_float(g4.y);
+      gv[2] = __uint_as_float(g4.z); gv[3] = __uint_as_float(g4.w);
+    } else {
 #pragma unroll
-    for (int e = 0; e < TC / 16; ++e) {
-      const int64_t v = v0 + 16 * e + u;
-      gv[e] = bload4f(gr, (grow >= 0 && v < c1) ? uint32_t((int64_t)grow * V + v) * 4u : kOutOfRange);
+      for (int k = 0; k < 4; ++k)
+        gv[k] = bload4f(gr, (grow >= 0 && vq + k < c1) ? uint32_t((int64_t)grow * V + vq + k) * 4u : kOutOfRange);
     }
     uint4 x[NS];
-    const uint32_t off = uint32_t(v0) * 64u + uint32_t(tid) * 16u;  // 64 columns x 16 rows
+    const uint32_t off = (prow + uint32_t(v0) + 4u * uint32_t(tid & 15)) * 4u;
 #pragma unroll
     for (int qq = 0; qq < NS; ++qq) x[qq] = bload16(pr[qq], off, 0);
     double sum[4] = {0.0, 0.0, 0.0, 0.0};
@@ -1077,27 +1093,32 @@ __global__ __launch_bounds__(kWideCombineThreads) void wide_stats_kernel(WideArg
       sum[2] += double(__uint_as_float(x[qq].z));
       sum[3] += double(__uint_as_float(x[qq].w));
     }
-    {
-      const int e = 4 * tid, col = e >> 4, row = e & 15;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) zt[col][row + k] = float(sum[k]);
-    }
+    for (int k = 0; k < 4; ++k) zt[4 * (tid & 15) + k][tid >> 4] = float(sum[k]);
     __syncthreads();  // zt holds tile v0
     if (rowok) {
+      float z[4];
 #pragma unroll
-      for (int e = 0; e < TC / 16; ++e) {
-        const int col = 16 * e + u;
-        const int64_t v = v0 + col;
+      for (int k = 0; k < 4; ++k) z[k] = zt[4 * u + k][ml];
+      if (quad) {
+        bstore16(make_uint4(__float_as_uint(z[0]), __float_as_uint(z[1]), __float_as_uint(z[2]),
+                            __float_as_uint(z[3])),
+                 lr, vq < c1 ? uint32_t((int64_t)m * V + vq) * 4u : kOutOfRange);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) bstore4f(z[k], lr, vq + k < c1 ? uint32_t((int64_t)m * V + vq + k) * 4u : kOutOfRange);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t v = vq + k;
         const bool vok = v < c1;
-        const float z = zt[col][ml];
-        bstore4f(z, lr, vok ? uint32_t((int64_t)m * V + v) * 4u : kOutOfRange);
-        const bool fin = fabsf(z) <= FLT_MAX;
+        const bool fin = fabsf(z[k]) <= FLT_MAX;
         if (vok && !fin) st.flags |= JSV_FLAG_INVALID;
-        const float ze = (vok && fin) ? z : -INFINITY;
+        const float ze = (vok && fin) ? z[k] : -INFINITY;
         if (ze > st.m) { st.top2 = st.m; st.idx = int(v); } else { st.top2 = fmaxf(st.top2, ze); }
         if (soft) fold(st.m, st.s, ze, c); else st.m = fmaxf(st.m, ze);
         if (grow >= 0) {
-          const float gq = gv[e];
+          const float gq = gv[k];
           const bool qf = fabsf(gq) <= FLT_MAX;
           if (vok && !qf) st.flags |= JSV_FLAG_INVALID;
           fold(st.mq, st.sq, (vok && qf) ? gq : -INFINITY, c);
