@@ -339,6 +339,24 @@ def test_score_k32_b4_d5120_fp8(qwen, dev):
     assert st["exact"] >= 3
 
 
+def test_score_split_d_ragged(dev):
+    """Scoring through the split-d LM head on a ragged vocabulary (V = 5003, two blocks of
+    d, 99 rows): both proposals, top-8, T = 1; the 4-byte access path of the combine."""
+    head = synth.random_head(5003, 2048, synth.BF16, seed=43)
+    case = Case(head, dev)
+    ws = jsv.new_workspace(case.gpu, 3, 32, 8)
+    st = new_stats()
+    for mode in (SOFT, POINT):
+        for seed in range(2):
+            say(f"score split-d V=5003 d=2048 B=3 K=32 mode={mode} seed={seed}")
+            blk = synth.make_block(head, 3, 32, 0.3, 1.0, seed=80 + seed)
+            hp = synth.predicted_hidden(blk.hidden, seed)
+            got, ref = run_score(case, hp, blk.draft_tokens, blk.draft_logits, 1.0, mode, 8, ws)
+            compare_score(got, ref, st)
+    say(f"  {st}")
+    assert st["exact"] >= 6
+
+
 def test_verify_qwen8b_k16_more_seeds(qwen, dev):
     """Eight more seeds of the benchmark block at T = 1 (softmax proposal): exact except
     at flagged near-ties."""
