@@ -180,7 +180,15 @@ size_t jsv_workspace_bytes(const jsv_lm_head* head, int32_t batch, int32_t K, in
   int nks = 0;
   if (check_head(head, &nks) != JSV_OK) return 0;
   if (batch < 1 || batch > kMaxB || K < 1 || K > kMaxK || top_n < 0 || top_n > kMaxTopN) return 0;
-  return needed_bytes(head, batch, K, top_n, true);
+  // Any call with at most `batch` requests and `K` drafts: a smaller block can need more
+  // (34..144 rows take the split-d LM head and its partial-product planes).
+  size_t most = 0;
+  for (int b = 1; b <= batch; ++b)
+    for (int k = 1; k <= K; ++k) {
+      const size_t n = needed_bytes(head, b, k, top_n, true);
+      if (n > most) most = n;
+    }
+  return most;
 }
 
 jsv_status jsv_lmhead_logits(const jsv_lm_head* head, const void* hidden, int64_t rows,

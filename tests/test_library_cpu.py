@@ -78,6 +78,11 @@ def test_workspace_holds_the_split_d_planes(lib):
     assert lib.jsv_workspace_bytes(ctypes.byref(d3), 2, 32, 8) >= 3 * V * 80 * 4
     d5 = head(vocab=V, hidden=5120)
     assert lib.jsv_workspace_bytes(ctypes.byref(d5), 4, 32, 8) >= 5 * V * 144 * 4
+    # a workspace sized for a larger block (264 rows: row passes) also covers the smaller
+    # blocks that take the split-d path
+    assert lib.jsv_workspace_bytes(ctypes.byref(bf), 8, 32, 8) >= n_wide
+    for b, k in [(1, 16), (2, 16), (4, 16), (4, 32), (8, 16), (8, 32)]:
+        assert lib.jsv_workspace_bytes(ctypes.byref(bf), 8, 32, 8) >= lib.jsv_workspace_bytes(ctypes.byref(bf), b, k, 8)
 
 
 def _verify(lib, h=None, **kw):
