@@ -339,6 +339,23 @@ def test_score_k32_b4_d5120_fp8(qwen, dev):
     assert st["exact"] >= 3
 
 
+def test_split_d_block_in_a_workspace_sized_for_the_largest_block(dev):
+    """A workspace sized for B = 8, K = 32 (264 rows: row passes) serves a B = 3, K = 32
+    block, which takes the split-d LM head and needs its planes."""
+    head = synth.random_head(5003, 2048, synth.BF16, seed=47)
+    case = Case(head, dev)
+    ws = jsv.new_workspace(case.gpu, 8, 32)
+    st = new_stats()
+    for T in (0.0, 1.0):
+        say(f"split-d B=3 K=32 in an 8 x 32 workspace, T={T}")
+        blk = synth.make_block(head, 3, 32, 0.3, T, seed=90)
+        got, ref = run_verify(case, blk, T, SOFT, 5, 6, ws)
+        compare_verify(got, ref, blk.draft_tokens.numpy(), st)
+        compare_logits(got["logits"], ref["logits"], st)
+    say(f"  {st}")
+    assert st["exact"] >= 4
+
+
 def test_score_split_d_ragged(dev):
     """Scoring through the split-d LM head on a ragged vocabulary (V = 5003, two blocks of
     d, 99 rows): both proposals, top-8, T = 1; the 4-byte access path of the combine."""
